@@ -1,0 +1,150 @@
+/*
+ * pkv.h — C ABI of a HIP library (gfx950 / MI355X) for attention over a paged,
+ * block-table-indexed KV cache.
+ *
+ * Conventions shared by every call:
+ *   - Pointers without a _h suffix are DEVICE pointers; _h pointers are host memory.
+ *     bf16 buffers are passed as void*, dense, row-major, 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every kernel is enqueued on it and the
+ *     call returns without synchronising. The library allocates no device memory: the caller owns
+ *     every buffer, including outputs and workspace.
+ *   - KV cache layout (K and V alike): [num_blocks, num_kv_heads, block_size, head_dim] bf16.
+ *     Token t of a sequence lives in physical block block_tables[b][t / block_size] at offset
+ *     t % block_size. Block tables are int32 [batch, max_blocks_per_seq], padded with -1; only the
+ *     first ceil(len / block_size) entries of a row are read.
+ *   - Query head h reads kv head h / (num_q_heads / num_kv_heads) (consecutive q heads share).
+ *   - Return value: PKV_OK, or an error code; on error nothing was enqueued. Device-side
+ *     preconditions (table contents, lengths, slots) are trusted for speed; the kernels clamp
+ *     every address they form to the buffers described by the size arguments, so a broken table
+ *     gives wrong numbers, never an out-of-bounds access. pkv_validate_block_tables_h checks them.
+ *   - Slots that hold no token (the tail of a sequence's last block, unused blocks) may hold any
+ *     bits, NaN included: they are excluded by length, never read into a result.
+ *
+ * Supported: head_dim in {64, 128, 256}; num_q_heads % num_kv_heads == 0; block_size a multiple
+ * of 16 up to 256; bf16 data, fp32 accumulation, bf16 output rounded to nearest even.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_E_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned buffer */
+  PKV_E_UNSUPPORTED = 2,      /* head_dim / block_size / grouping not built */
+  PKV_E_BAD_TABLE = 3,        /* checked-mode table validation failed */
+  PKV_E_WORKSPACE_TOO_SMALL = 4,
+  PKV_E_HIP = 5               /* a HIP launch reported an error */
+};
+
+/* Human-readable name of a status code (static storage). */
+const char* pkv_status_string(int status);
+
+/*
+ * reshape_and_cache — scatter new tokens' K/V rows into their cache slots.
+ * Defined by the vLLM-derived paged_attn.py page, PagedAttention.write_to_paged_cache: key and
+ * value [T, Hkv, D] are written to the slot each token's flattened slot_mapping names, where a
+ * slot is physical_block * block_size + offset.
+ *
+ *   k, v            [num_tokens, num_kv_heads, head_dim] bf16, read only.
+ *   k_cache,v_cache [num_blocks, num_kv_heads, block_size, head_dim] bf16, written in place.
+ *   slot_mapping    [num_tokens] int64. A negative slot skips the token. Slots >= num_blocks *
+ *                   block_size are skipped as well (a caller error). Duplicate slots are a caller
+ *                   error with an unspecified winner.
+ * The copy is bit-exact. Slots not named keep their contents. num_tokens == 0 is a no-op.
+ */
+int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                          const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks, void* stream);
+
+/*
+ * Workspace bytes paged_attn_decode needs for the given shape and partition choice (0 when the
+ * direct, single-pass path is taken). partition_tokens: 0 = direct, > 0 = split-KV with that many
+ * tokens per partition, -1 = the library's choice (the same choice paged_attn_decode makes).
+ */
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_seq_len, int32_t partition_tokens);
+
+/*
+ * paged_attn_decode — one query token per sequence against its paged KV cache.
+ * Defined by the vLLM-derived paged_attn.py page (PagedAttention._forward_decode_pytorch and
+ * forward_decode): out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over tokens [0, seq_lens[b]),
+ * K_b/V_b read through block_tables[b]. seq_lens[b] == 0 gives a zero row. The split-KV form cuts
+ * each sequence into partitions of partition_tokens (vLLM uses 512) whose running max / exp-sum /
+ * partial output are merged by log-sum-exp in a second kernel, as the same page's V2 path does.
+ *
+ *   q            [batch, num_q_heads, head_dim] bf16.
+ *   out          [batch, num_q_heads, head_dim] bf16, fully overwritten.
+ *   lse          optional [batch, num_q_heads] fp32: natural-log log-sum-exp of the scaled scores
+ *                (-inf for an empty sequence). NULL to skip.
+ *   block_tables [batch, max_blocks_per_seq] int32; seq_lens [batch] int32.
+ *   max_seq_len  host hint: must be >= every seq_lens[b]; sizes the split grid. Lengths are also
+ *                clamped to max_blocks_per_seq * block_size.
+ *   partition_tokens  0 = direct; > 0 = split (a multiple of 32); -1 = library choice.
+ *   workspace    device scratch of at least pkv_decode_workspace_bytes(...) bytes (may be NULL
+ *                when that is 0). Its contents need no initialisation.
+ */
+int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, void* out, float* lse,
+                          int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t max_seq_len, float scale, int32_t partition_tokens, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * ragged_prefill — N requests' attention in one launch over contiguous ragged rows.
+ * Defined by the spark_runtime/flashinfer.rs page, ragged_prefill_bf16_hd256 and its CPU-reference
+ * test: request b's queries are rows qo_indptr[b]..qo_indptr[b+1] of q, its keys/values rows
+ * kv_indptr[b]..kv_indptr[b+1] of k/v; with causal != 0, query row i of a request sees key j iff
+ * j <= i + (kv_len - qo_len) (bottom-right alignment). A row that sees no key is zero.
+ *
+ *   q, out   [qo_indptr_h[batch], num_q_heads, head_dim] bf16.
+ *   k, v     [kv_indptr_h[batch], num_kv_heads, head_dim] bf16.
+ *   qo_indptr, kv_indptr        device [batch + 1] int32 prefix sums (read by the kernel).
+ *   qo_indptr_h, kv_indptr_h    host copies of the same (sizes the launch; no device sync).
+ */
+int pkv_ragged_prefill(const void* q, const void* k, const void* v, void* out,
+                       const int32_t* qo_indptr, const int32_t* kv_indptr,
+                       const int32_t* qo_indptr_h, const int32_t* kv_indptr_h, int32_t batch,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t causal,
+                       float scale, void* stream);
+
+/*
+ * paged_prefill — prefill whose keys/values come through the block table (chunked prefill over a
+ * cached prefix). Defined by the vLLM-derived paged_attn.py page, _forward_prefix_pytorch: the
+ * cached prefix is visible to every new row; the new chunk (already written to the cache by
+ * reshape_and_cache) is causal. Request b's queries are rows qo_indptr[b]..qo_indptr[b+1] of q;
+ * its keys are cached tokens [0, kv_lens[b]); query i sees key j iff j <= kv_lens[b] - qo_len + i
+ * when causal != 0.
+ *
+ *   q, out       [qo_indptr_h[batch], num_q_heads, head_dim] bf16.
+ *   block_tables [batch, max_blocks_per_seq] int32; kv_lens device [batch] int32.
+ *   qo_indptr    device [batch + 1]; qo_indptr_h, kv_lens_h host copies.
+ */
+int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* qo_indptr, const int32_t* kv_lens,
+                      const int32_t* qo_indptr_h, const int32_t* kv_lens_h, void* out, int32_t batch,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t causal, float scale,
+                      void* stream);
+
+/*
+ * Checked-mode validation of block tables on the host, following the libmir-cuda page
+ * (PagedAttentionBf16::validate_table): every sequence's table must hold its declared tokens
+ * (ceil(len / block_size) <= max_blocks_per_seq) and every entry a sequence reads must name an
+ * existing physical block (0 <= id < num_blocks). Returns PKV_OK, PKV_E_BAD_TABLE, or
+ * PKV_E_INVALID_ARGUMENT (null pointers, negative sizes or lengths). Host memory only.
+ */
+int pkv_validate_block_tables_h(const int32_t* block_tables_h, const int32_t* seq_lens_h,
+                                int32_t batch, int32_t max_blocks_per_seq, int32_t block_size,
+                                int32_t num_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

@@ -1,0 +1,257 @@
+// C ABI of the paged-KV attention library: argument checks, path choice, launches.
+// Every check runs before anything is enqueued, so an error status means nothing was launched.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/pkv.h"
+#include "kernels.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+
+bool block_size_ok(int bs) { return bs >= 16 && bs <= 256 && bs % 16 == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_E_HIP; }
+
+// Auto choice of the decode path. A direct launch gives one work-group per (sequence, kv head,
+// q-head group); when that is too few to fill 256 CUs several times over and sequences are
+// longer than one partition, split-KV with 512-token partitions (the vLLM page's _PARTITION_SIZE).
+constexpr int kDefaultPartition = 512;
+constexpr int kDirectMinGroups = 1024;
+
+int resolve_partition(int batch, int num_q_heads, int num_kv_heads, int max_seq_len,
+                      int partition_tokens) {
+  if (partition_tokens >= 0) return partition_tokens;
+  const int G = num_q_heads / num_kv_heads;
+  const long groups = (long)batch * num_kv_heads * ((G + 15) / 16);
+  if (max_seq_len > kDefaultPartition && groups < kDirectMinGroups) return kDefaultPartition;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_E_INVALID_ARGUMENT: return "invalid argument";
+    case PKV_E_UNSUPPORTED: return "unsupported configuration";
+    case PKV_E_BAD_TABLE: return "bad block table";
+    case PKV_E_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PKV_E_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                          const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return PKV_E_INVALID_ARGUMENT;
+  if (head_dim <= 0 || head_dim % 8 != 0 || block_size <= 0) return PKV_E_INVALID_ARGUMENT;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_E_INVALID_ARGUMENT;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_E_INVALID_ARGUMENT;
+  return hip_status(pkv::launch_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens,
+                                                  num_kv_heads, head_dim, block_size, num_blocks,
+                                                  (hipStream_t)stream));
+}
+
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_seq_len, int32_t partition_tokens) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0)
+    return 0;
+  if (num_q_heads % num_kv_heads != 0) return 0;
+  const int pt = resolve_partition(batch, num_q_heads, num_kv_heads, max_seq_len, partition_tokens);
+  return pkv::decode_workspace_layout(batch, num_q_heads, head_dim, max_seq_len, pt).total;
+}
+
+int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, void* out, float* lse,
+                          int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t max_seq_len, float scale, int32_t partition_tokens, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_seq_len < 0 || partition_tokens < -1)
+    return PKV_E_INVALID_ARGUMENT;
+  if (num_q_heads % num_kv_heads != 0) return PKV_E_INVALID_ARGUMENT;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PKV_E_UNSUPPORTED;
+  if (partition_tokens > 0 && partition_tokens % 32 != 0) return PKV_E_UNSUPPORTED;
+  if (batch == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PKV_E_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return PKV_E_INVALID_ARGUMENT;
+  const int G = num_q_heads / num_kv_heads;
+  const long ygrid = (long)num_kv_heads * ((G + 15) / 16);
+  if (batch > 65535 || ygrid > 65535) return PKV_E_UNSUPPORTED;
+
+  pkv::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.scale = scale;
+  a.partition_tokens =
+      resolve_partition(batch, num_q_heads, num_kv_heads, max_seq_len, partition_tokens);
+  if (a.partition_tokens > 0) {
+    const pkv::DecodeWorkspaceLayout wl = pkv::decode_workspace_layout(
+        batch, num_q_heads, head_dim, max_seq_len, a.partition_tokens);
+    if (wl.max_partitions > 65535) return PKV_E_UNSUPPORTED;
+    if (workspace == nullptr || workspace_bytes < wl.total) return PKV_E_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return PKV_E_INVALID_ARGUMENT;
+    char* ws = static_cast<char*>(workspace);
+    a.o_part = reinterpret_cast<float*>(ws + wl.o_off);
+    a.m_part = reinterpret_cast<float*>(ws + wl.m_off);
+    a.l_part = reinterpret_cast<float*>(ws + wl.l_off);
+    a.max_partitions = wl.max_partitions;
+  }
+  return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+static int check_prefill_common(const void* q, const void* out, const int32_t* qo_indptr,
+                                const int32_t* qo_indptr_h, int32_t batch, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int* max_qo, int* total_q) {
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0) return PKV_E_INVALID_ARGUMENT;
+  if (num_q_heads % num_kv_heads != 0) return PKV_E_INVALID_ARGUMENT;
+  if (!head_dim_ok(head_dim)) return PKV_E_UNSUPPORTED;
+  if (batch == 0) {
+    *max_qo = 0;
+    *total_q = 0;
+    return PKV_OK;
+  }
+  if (!qo_indptr_h || !qo_indptr) return PKV_E_INVALID_ARGUMENT;
+  if (qo_indptr_h[0] != 0) return PKV_E_INVALID_ARGUMENT;
+  int mx = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int n = qo_indptr_h[b + 1] - qo_indptr_h[b];
+    if (n < 0) return PKV_E_INVALID_ARGUMENT;
+    if (n > mx) mx = n;
+  }
+  *max_qo = mx;
+  *total_q = qo_indptr_h[batch];
+  if (*total_q > 0 && (!q || !out)) return PKV_E_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(out)) return PKV_E_INVALID_ARGUMENT;
+  if (batch > 65535) return PKV_E_UNSUPPORTED;
+  return PKV_OK;
+}
+
+int pkv_ragged_prefill(const void* q, const void* k, const void* v, void* out,
+                       const int32_t* qo_indptr, const int32_t* kv_indptr,
+                       const int32_t* qo_indptr_h, const int32_t* kv_indptr_h, int32_t batch,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t causal,
+                       float scale, void* stream) {
+  int max_qo = 0, total_q = 0;
+  int st = check_prefill_common(q, out, qo_indptr, qo_indptr_h, batch, num_q_heads, num_kv_heads,
+                                head_dim, &max_qo, &total_q);
+  if (st != PKV_OK || batch == 0) return st;
+  if (!kv_indptr_h || !kv_indptr) return PKV_E_INVALID_ARGUMENT;
+  if (kv_indptr_h[0] != 0) return PKV_E_INVALID_ARGUMENT;
+  for (int b = 0; b < batch; ++b)
+    if (kv_indptr_h[b + 1] < kv_indptr_h[b]) return PKV_E_INVALID_ARGUMENT;
+  const int64_t total_kv = kv_indptr_h[batch];
+  if (total_kv > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return PKV_E_INVALID_ARGUMENT;
+  if (total_q == 0) return PKV_OK;
+  pkv::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.qo_indptr = qo_indptr;
+  a.kv_indptr = kv_indptr;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.max_qo_len = max_qo;
+  a.total_q = total_q;
+  a.total_kv = total_kv;
+  const hipError_t e = pkv::launch_ragged_prefill(a, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return PKV_E_UNSUPPORTED;
+  return hip_status(e);
+}
+
+int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* qo_indptr, const int32_t* kv_lens,
+                      const int32_t* qo_indptr_h, const int32_t* kv_lens_h, void* out, int32_t batch,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t causal, float scale,
+                      void* stream) {
+  int max_qo = 0, total_q = 0;
+  int st = check_prefill_common(q, out, qo_indptr, qo_indptr_h, batch, num_q_heads, num_kv_heads,
+                                head_dim, &max_qo, &total_q);
+  if (st != PKV_OK || batch == 0) return st;
+  if (!block_size_ok(block_size)) return PKV_E_UNSUPPORTED;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PKV_E_INVALID_ARGUMENT;
+  if (!kv_lens_h || !kv_lens || !block_tables || !k_cache || !v_cache) return PKV_E_INVALID_ARGUMENT;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_E_INVALID_ARGUMENT;
+  for (int b = 0; b < batch; ++b) {
+    if (kv_lens_h[b] < 0) return PKV_E_INVALID_ARGUMENT;
+    if ((int64_t)kv_lens_h[b] > (int64_t)max_blocks_per_seq * block_size) return PKV_E_BAD_TABLE;
+  }
+  if (total_q == 0) return PKV_OK;
+  pkv::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.qo_indptr = qo_indptr;
+  a.kv_lens = kv_lens;
+  a.block_tables = block_tables;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.max_qo_len = max_qo;
+  a.total_q = total_q;
+  const hipError_t e = pkv::launch_paged_prefill(a, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return PKV_E_UNSUPPORTED;
+  return hip_status(e);
+}
+
+int pkv_validate_block_tables_h(const int32_t* block_tables_h, const int32_t* seq_lens_h,
+                                int32_t batch, int32_t max_blocks_per_seq, int32_t block_size,
+                                int32_t num_blocks) {
+  if (batch < 0 || max_blocks_per_seq < 0 || block_size <= 0 || num_blocks < 0)
+    return PKV_E_INVALID_ARGUMENT;
+  if (batch > 0 && (!seq_lens_h || (max_blocks_per_seq > 0 && !block_tables_h)))
+    return PKV_E_INVALID_ARGUMENT;
+  for (int b = 0; b < batch; ++b)
+    if (seq_lens_h[b] < 0) return PKV_E_INVALID_ARGUMENT;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t need = ((int64_t)seq_lens_h[b] + block_size - 1) / block_size;
+    if (need > max_blocks_per_seq) return PKV_E_BAD_TABLE;
+    const int32_t* row = block_tables_h + (size_t)b * max_blocks_per_seq;
+    for (int64_t j = 0; j < need; ++j)
+      if (row[j] < 0 || row[j] >= num_blocks) return PKV_E_BAD_TABLE;
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

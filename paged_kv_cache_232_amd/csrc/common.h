@@ -1,0 +1,75 @@
+// Internal helpers shared by the HIP kernels of the paged-KV attention library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16x16x32 bf16 MFMA, fp32 accumulate. Operand layout (wave64):
+//   A [16 x 32]: lane l holds A[l % 16][8 * (l / 16) + j], j = 0..7
+//   B [32 x 16]: lane l holds B[8 * (l / 16) + j][l % 16]
+//   C [16 x 16]: lane l holds C[4 * (l / 16) + r][l % 16], r = 0..3
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x16 bf16 MFMA, fp32 accumulate. Operand layout (wave64):
+//   A [32 x 16]: lane l holds A[l % 32][8 * (l / 32) + j]
+//   B [16 x 32]: lane l holds B[8 * (l / 32) + j][l % 32]
+//   C [32 x 32]: lane l holds C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32], r = 0..15
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
+  u32x4 r;
+  r[0] = pack_bf16x2(v[0], v[1]);
+  r[1] = pack_bf16x2(v[2], v[3]);
+  r[2] = pack_bf16x2(v[4], v[5]);
+  r[3] = pack_bf16x2(v[6], v[7]);
+  return as_bf16x8(r);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+template <typename T>
+__device__ __forceinline__ T clampi(T x, T lo, T hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+}  // namespace pkv

@@ -1,0 +1,381 @@
+// Paged decode attention: one query token per sequence against its block-table-indexed KV cache.
+//
+// What is computed (vLLM-derived paged_attn.py page, PagedAttention._forward_decode_pytorch and
+// forward_decode): out[b, h] = softmax(scale * q[b, h] . K^T) V over the sequence's tokens, with
+// a running max / exp-sum / rescaled output carried across tiles, and (split-KV, the page's V2
+// path) 512-token partitions whose statistics a second kernel merges by log-sum-exp.
+//
+// MI355X design. Decode moves every K/V byte exactly once, so the kernel is an HBM stream:
+//   * work-group = 4 waves on one (sequence, kv head, q-head group of <= 16, partition);
+//     each wave walks 32-token chunks (two 16-token half pages) round robin and keeps its own
+//     running (m, l, O); the four are combined through LDS at the end;
+//   * QK^T on a 16x16x32 bf16 MFMA with the K half page as the A operand (rows = 16 tokens, loaded
+//     straight from HBM in 16-byte pieces) and the GQA group's q rows as B (16 columns);
+//   * the score tile lands in the layout the PV MFMA needs for its B operand: each lane already
+//     holds 8 probabilities of one head, so P never moves between lanes;
+//   * V is read from HBM in fully contiguous 1 KiB wave loads, staged row-major in a per-wave
+//     LDS tile with an 8-byte row pad, and read back column-wise as the PV MFMA's A operand (V^T);
+//   * softmax runs in the log2 domain (scale * log2 e folded into one multiply, v_exp_f32);
+//     slots past the sequence length are masked by selection (their bits may be NaN).
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = kDecodeWaves * kWave;
+
+template <int D>
+struct DecodeCfg {
+  static constexpr int KK = D / 32;           // 32-wide d slices of the QK MFMA
+  static constexpr int MT = D / 16;           // 16-row d tiles of the PV MFMA
+  static constexpr int VU = D / 32;           // 16-byte V units per lane per half page
+  static constexpr int RS = 2 * D + 8;        // LDS bytes per staged V row (8-byte pad)
+  static constexpr int WAVE_LDS = 32 * RS;    // one wave's 32-row V tile
+  static_assert(WAVE_LDS >= D * 16 * 4, "combine buffer must fit in a wave's V tile");
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+template <int D, bool SPLIT>
+__global__ void __launch_bounds__(kDecodeThreads)
+decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+              const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables,
+              const int32_t* __restrict__ lens, uint16_t* __restrict__ out,
+              float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ m_part,
+              float* __restrict__ l_part, int Hq, int Hkv, int G, int n_hg, int BS, int NB,
+              int max_blocks, int PT, int Pmax, float scale_log2) {
+  using C = DecodeCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[kDecodeWaves * C::WAVE_LDS];
+  __shared__ float sm_m[kDecodeWaves][16];
+  __shared__ float sm_l[kDecodeWaves][16];
+
+  const int p = blockIdx.x;
+  const int kh = blockIdx.y / n_hg;
+  const int hg = blockIdx.y - kh * n_hg;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int col = lane & 15;  // head column of the MFMA tiles
+  const int qg = lane >> 4;   // lane group 0..3
+
+  int L = clampi(lens[b], 0, max_blocks * BS);
+  int t_begin = 0, t_end = L;
+  if constexpr (SPLIT) {
+    L = min(L, Pmax * PT);
+    t_begin = p * PT;
+    if (t_begin >= L) return;  // uniform over the work-group
+    t_end = min(L, t_begin + PT);
+  }
+
+  const int gcol = hg * 16 + col;
+  const bool col_ok = gcol < G;
+  const int hq = kh * G + min(gcol, G - 1);
+
+  // B operand of QK: q[hq][kk*32 + 8*qg .. +8]
+  bf16x8 qreg[C::KK];
+  {
+    const uint16_t* qp = q + ((size_t)b * Hq + hq) * D + 8 * qg;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      u32x4 v = load16(qp + kk * 32);
+      if (!col_ok) v = u32x4{0, 0, 0, 0};
+      qreg[kk] = as_bf16x8(v);
+    }
+  }
+
+  f32x4 o[C::MT];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  char* vbuf = smem + w * C::WAVE_LDS;
+  const uint16_t* vl = reinterpret_cast<const uint16_t*>(vbuf);
+  const int n_chunks = (t_end - t_begin + 31) >> 5;
+  const int32_t* trow = tables + (size_t)b * max_blocks;
+  const size_t head_stride = (size_t)BS * D;
+  const size_t block_stride = (size_t)Hkv * head_stride;
+
+  for (int c = w; c < n_chunks; c += kDecodeWaves) {
+    const int cs = t_begin + c * 32;
+    size_t base[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int tok0 = cs + 16 * hh;
+      const int tk = tok0 < t_end ? tok0 : cs;  // an all-masked half page re-reads a valid one
+      const int blk = clampi(trow[tk / BS], 0, NB - 1);
+      base[hh] = (size_t)blk * block_stride + (size_t)kh * head_stride + (size_t)(tk % BS) * D;
+    }
+    u32x4 kr[2][C::KK];
+    u32x4 vr[2][C::VU];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk)
+        kr[hh][kk] = load16(kc + base[hh] + (size_t)col * D + kk * 32 + 8 * qg);
+#pragma unroll
+      for (int i = 0; i < C::VU; ++i) vr[hh][i] = load16(vc + base[hh] + (size_t)(i * 64 + lane) * 8);
+    }
+
+    // S^T[token][head] for the two half pages
+    f32x4 s[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) s[hh] = mfma16(as_bf16x8(kr[hh][kk]), qreg[kk], s[hh]);
+    }
+
+    // stage V rows in LDS; rows past the end are zeroed (select, so NaN slack never leaks)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int i = 0; i < C::VU; ++i) {
+        const int u = i * 64 + lane;
+        const int row = u / (D / 8);
+        const int cu = u - row * (D / 8);
+        u32x4 val = vr[hh][i];
+        if (cs + 16 * hh + row >= t_end) val = u32x4{0, 0, 0, 0};
+        char* dst = vbuf + (16 * hh + row) * C::RS + cu * 16;
+        *reinterpret_cast<u32x2*>(dst) = u32x2{val[0], val[1]};
+        *reinterpret_cast<u32x2*>(dst + 8) = u32x2{val[2], val[3]};
+      }
+    }
+
+    // scores in log2 units, masked past the end
+    float sv[8];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = cs + 16 * hh + 4 * qg + r;
+        const float x = s[hh][r] * scale_log2;
+        sv[hh * 4 + r] = tok < t_end ? x : -INFINITY;
+      }
+    float mx = sv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = fast_exp2(m_run - m_new);
+    float pv[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pv[j] = fast_exp2(sv[j] - m_new);
+      ps += pv[j];
+    }
+    l_run = l_run * corr + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) o[mt] *= corr;
+    // B operand of PV: k-index 8*qg + j <-> token 16*(j/4) + 4*qg + j%4, exactly this lane's scores
+    const bf16x8 pb = pack_bf16x8(pv);
+
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+      const int d = mt * 16 + col;
+      u32x4 a;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j0 = 2 * jj, j1 = 2 * jj + 1;
+        const int r0 = 16 * (j0 >> 2) + 4 * qg + (j0 & 3);
+        const int r1 = 16 * (j1 >> 2) + 4 * qg + (j1 & 3);
+        const uint32_t lo = vl[r0 * (C::RS / 2) + d];
+        const uint32_t hi = vl[r1 * (C::RS / 2) + d];
+        a[jj] = lo | (hi << 16);
+      }
+      o[mt] = mfma16(as_bf16x8(a), pb, o[mt]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // lane-group partial sums -> per-column sums (m_run is already uniform per column)
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  __syncthreads();  // every wave is done with its V tile; reuse it for O^T [d][16]
+  float* obuf = reinterpret_cast<float*>(vbuf);
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) obuf[(mt * 16 + 4 * qg + r) * 16 + col] = o[mt][r];
+  if (lane < 16) {
+    sm_m[w][lane] = m_run;
+    sm_l[w][lane] = l_run;
+  }
+  __syncthreads();
+
+  const int t = threadIdx.x;
+  const int oc = t >> 4;     // head column
+  const int dpart = t & 15;  // this thread's D/16 consecutive outputs
+  if (hg * 16 + oc >= G) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w2 = 0; w2 < kDecodeWaves; ++w2) M = fmaxf(M, sm_m[w2][oc]);
+  float f[kDecodeWaves];
+  float lsum = 0.f;
+#pragma unroll
+  for (int w2 = 0; w2 < kDecodeWaves; ++w2) {
+    const float mw = sm_m[w2][oc];
+    f[w2] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+    lsum += f[w2] * sm_l[w2][oc];
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  constexpr int DPT = D / 16;
+  float acc[DPT];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) {
+    const int d = dpart * DPT + i;
+    float a = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kDecodeWaves; ++w2)
+      a += f[w2] * reinterpret_cast<const float*>(smem + w2 * C::WAVE_LDS)[d * 16 + oc];
+    acc[i] = a * inv;
+  }
+  const int hout = kh * G + hg * 16 + oc;
+  if constexpr (SPLIT) {
+    const size_t pi = ((size_t)b * Hq + hout) * Pmax + p;
+    float* op = o_part + pi * D + dpart * DPT;
+#pragma unroll
+    for (int i = 0; i < DPT; i += 4)
+      *reinterpret_cast<f32x4*>(op + i) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
+    if (dpart == 0) {
+      m_part[pi] = M;
+      l_part[pi] = lsum;
+    }
+  } else {
+    uint16_t* op = out + ((size_t)b * Hq + hout) * D + dpart * DPT;
+#pragma unroll
+    for (int i = 0; i < DPT; i += 4)
+      *reinterpret_cast<u32x2*>(op + i) =
+          u32x2{pack_bf16x2(acc[i], acc[i + 1]), pack_bf16x2(acc[i + 2], acc[i + 3])};
+    if (lse != nullptr && dpart == 0)
+      lse[(size_t)b * Hq + hout] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+// Log-sum-exp merge of split partials: one work-group per (q head, sequence).
+template <int D>
+__global__ void __launch_bounds__(256)
+decode_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ m_part,
+                    const float* __restrict__ l_part, const int32_t* __restrict__ lens,
+                    uint16_t* __restrict__ out, float* __restrict__ lse, int Hq, int max_blocks,
+                    int BS, int PT, int Pmax) {
+  constexpr int U = D / 4;       // float4 units per partial row
+  constexpr int NG = 256 / U;    // partition groups
+  __shared__ float red[4];
+  __shared__ f32x4 red4[NG][U];
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int t = threadIdx.x;
+  int L = clampi(lens[b], 0, max_blocks * BS);
+  L = min(L, Pmax * PT);
+  const int P = (L + PT - 1) / PT;
+  const size_t pi0 = ((size_t)b * Hq + h) * Pmax;
+
+  float M = -INFINITY;
+  for (int p = t; p < P; p += 256) M = fmaxf(M, m_part[pi0 + p]);
+  M = wave_max(M);
+  if ((t & 63) == 0) red[t >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float S = 0.f;
+  for (int p = t; p < P; p += 256) S += l_part[pi0 + p] * fast_exp2(m_part[pi0 + p] - M);
+  S = wave_sum(S);
+  if ((t & 63) == 0) red[t >> 6] = S;
+  __syncthreads();
+  S = red[0] + red[1] + red[2] + red[3];
+
+  const int u = t % U;
+  const int g = t / U;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = g; p < P; p += NG) {
+    const float wgt = l_part[pi0 + p] * fast_exp2(m_part[pi0 + p] - M);
+    acc += wgt * reinterpret_cast<const f32x4*>(o_part + (pi0 + p) * D)[u];
+  }
+  red4[g][u] = acc;
+  __syncthreads();
+  if (g == 0) {
+    f32x4 sum = red4[0][u];
+#pragma unroll
+    for (int gg = 1; gg < NG; ++gg) sum += red4[gg][u];
+    const float inv = S > 0.f ? 1.f / S : 0.f;
+    sum *= inv;
+    *reinterpret_cast<u32x2*>(out + ((size_t)b * Hq + h) * D + u * 4) =
+        u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+    if (lse != nullptr && u == 0)
+      lse[(size_t)b * Hq + h] = S > 0.f ? (M + __log2f(S)) * kLn2 : -INFINITY;
+  }
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DecodeWorkspaceLayout decode_workspace_layout(int batch, int num_q_heads, int head_dim,
+                                              int max_seq_len, int partition_tokens) {
+  DecodeWorkspaceLayout w{0, 0, 0, 0, 0};
+  if (partition_tokens <= 0) return w;
+  const int P = max_seq_len > 0 ? (max_seq_len + partition_tokens - 1) / partition_tokens : 1;
+  const size_t rows = (size_t)batch * num_q_heads * P;
+  w.max_partitions = P;
+  w.o_off = 0;
+  w.m_off = align256(rows * head_dim * sizeof(float));
+  w.l_off = w.m_off + align256(rows * sizeof(float));
+  w.total = w.l_off + align256(rows * sizeof(float));
+  return w;
+}
+
+template <int D>
+static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int n_hg = (G + 15) / 16;
+  const float scale_log2 = a.scale * kLog2e;
+  const dim3 block(kDecodeThreads);
+  if (a.partition_tokens > 0) {
+    const dim3 grid(a.max_partitions, a.num_kv_heads * n_hg, a.batch);
+    hipLaunchKernelGGL((decode_kernel<D, true>), grid, block, 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache,
+                       a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, a.o_part, a.m_part,
+                       a.l_part, a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size,
+                       a.num_blocks, a.max_blocks_per_seq, a.partition_tokens, a.max_partitions,
+                       scale_log2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.num_q_heads, a.batch), dim3(256), 0,
+                       stream, a.o_part, a.m_part, a.l_part, a.seq_lens, (uint16_t*)a.out, a.lse,
+                       a.num_q_heads, a.max_blocks_per_seq, a.block_size, a.partition_tokens,
+                       a.max_partitions);
+    return hipGetLastError();
+  }
+  const dim3 grid(1, a.num_kv_heads * n_hg, a.batch);
+  hipLaunchKernelGGL((decode_kernel<D, false>), grid, block, 0, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache,
+                     a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, nullptr, nullptr,
+                     nullptr, a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size, a.num_blocks,
+                     a.max_blocks_per_seq, 0, 1, scale_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return launch_decode_d<64>(a, stream);
+    case 128: return launch_decode_d<128>(a, stream);
+    case 256: return launch_decode_d<256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pkv

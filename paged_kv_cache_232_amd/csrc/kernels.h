@@ -1,0 +1,67 @@
+// Internal launchers, one per kernel family. Each validates nothing: the C ABI layer in api.cpp
+// checks arguments first and only then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                                    int head_dim, int block_size, int num_blocks,
+                                    hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  int batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq;
+  int max_seq_len;
+  float scale;
+  int partition_tokens;  // 0 = direct, > 0 = split
+  // split workspace (null for direct)
+  float* o_part;
+  float* m_part;
+  float* l_part;
+  int max_partitions;
+};
+
+// Split-KV workspace layout for a given shape: o [B, Hq, P, D] f32, m and l [B, Hq, P] f32, each
+// region 256-byte aligned.
+struct DecodeWorkspaceLayout {
+  size_t o_off, m_off, l_off, total;
+  int max_partitions;
+};
+DecodeWorkspaceLayout decode_workspace_layout(int batch, int num_q_heads, int head_dim,
+                                              int max_seq_len, int partition_tokens);
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;        // contiguous [Tkv, Hkv, D] (ragged) or k_cache (paged)
+  const void* v;
+  void* out;
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;     // ragged only
+  const int32_t* kv_lens;       // paged only
+  const int32_t* block_tables;  // paged only
+  int batch, num_q_heads, num_kv_heads, head_dim;
+  int block_size, num_blocks, max_blocks_per_seq;  // paged only
+  int causal;
+  float scale;
+  int max_qo_len;   // host-side maximum of the q lengths (sizes the grid)
+  int total_q;      // rows of q / out
+  int64_t total_kv; // rows of k / v (ragged only)
+};
+
+hipError_t launch_ragged_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pkv
