@@ -1,10 +1,296 @@
-// Ragged and paged prefill attention (MFMA). Not built yet: both launchers report "not supported".
+// Ragged (varlen) and paged prefill attention on bf16 MFMA.
+//
+// What is computed: for request b, query row i (rows qo_indptr[b]..qo_indptr[b+1] of q) attends
+// to its keys 0..kv_len-1 (contiguous rows kv_indptr[b].. of k/v, or cached tokens read through the
+// block table); with causal masking, row i sees key j iff j <= i + (kv_len - qo_len). Sources: the
+// spark_runtime/flashinfer.rs page (ragged_prefill_bf16_hd256 and its CPU-reference test) and the
+// vLLM-derived paged_attn.py page (_forward_prefix_pytorch: cached prefix unmasked, chunk causal).
+//
+// MI355X design (a dense contraction, so MFMA-bound):
+//   * work-group = 4 waves; tile = 128 query rows of one q head (32 rows per wave);
+//   * K and V tiles of BN keys are staged row-major in LDS, loaded with 16-byte vector loads and
+//     prefetched into registers one tile ahead;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the wave's Q rows held in
+//     registers for the whole kernel), so each lane holds 16 keys of ONE query: the row max needs
+//     one cross-lane step, and the lane's probabilities are already the B operand of
+//     O^T += V^T P^T with no lane exchange;
+//   * softmax in the log2 domain; causal kv tiles above the diagonal are skipped, only tiles that
+//     cross the diagonal or the ragged end are masked;
+//   * q heads are mapped to block x so that the work-groups sharing one kv head land on one XCD
+//     (its L2 then serves the K/V re-reads of every q tile and every head of the group);
+//   * q tiles are issued last-first (the longest causal rows start first).
+#include <math.h>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace pkv {
 
-hipError_t launch_ragged_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_paged_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillThreads = kPrefillWaves * kWave;
+constexpr int kBM = 32 * kPrefillWaves;  // query rows per work-group
+
+template <int D>
+struct PrefillCfg {
+  static constexpr int BN = (D >= 256) ? 32 : 64;   // keys per kv tile
+  static constexpr int KS = D / 16;                 // 16-wide d steps of QK^T
+  static constexpr int MT = BN / 32;                // 32-key tiles of S^T
+  static constexpr int PS = BN / 16;                // 16-key steps of PV
+  static constexpr int DT = D / 32;                 // 32-wide d tiles of O^T
+  static constexpr int RSE = D + 8;                 // LDS row stride in elements (16-byte pad)
+  static constexpr int UPR = D / 8;                 // 16-byte units per row
+  static constexpr int UNITS = BN * UPR;            // units per tile (K or V)
+  static constexpr int UPT = UNITS / kPrefillThreads;  // units per thread
+  static_assert(UNITS % kPrefillThreads == 0, "tile units must divide evenly");
+};
+
+struct RaggedLoader {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t row0;   // first kv row of the request
+  int Hkv, kh, D;
+  __device__ __forceinline__ size_t row_offset(int n) const {
+    return ((size_t)(row0 + n) * Hkv + kh) * D;
+  }
+};
+
+struct PagedLoader {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* trow;  // this request's block-table row
+  int Hkv, kh, D, BS, NB;
+  __device__ __forceinline__ size_t row_offset(int n) const {
+    const int blk = clampi(trow[n / BS], 0, NB - 1);
+    return (((size_t)blk * Hkv + kh) * BS + (n % BS)) * D;
+  }
+};
+
+template <int D, bool PAGED>
+__global__ void __launch_bounds__(kPrefillThreads)
+prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+               const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
+               const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
+               const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ tables,
+               int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
+               int xcd_heads) {
+  using C = PrefillCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::BN * C::RSE];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[C::BN * C::RSE];
+
+  // block x -> q head: heads sharing a kv head go to the same XCD (round-robin x % 8)
+  int h = blockIdx.x;
+  if (xcd_heads > 0) h = (blockIdx.x & 7) * xcd_heads + (blockIdx.x >> 3);
+  const int b = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int kh = h / G;
+
+  const int q0 = qo_indptr[b];
+  const int qo = qo_indptr[b + 1] - q0;
+  int kv;
+  int64_t kv0 = 0;
+  if constexpr (PAGED) {
+    kv = clampi(kv_lens[b], 0, max_blocks * BS);
+  } else {
+    kv0 = kv_indptr[b];
+    kv = kv_indptr[b + 1] - (int)kv0;
+  }
+  const int n_qt = (qo + kBM - 1) / kBM;
+  const int qt = n_qt - 1 - (int)blockIdx.z;  // last tile first
+  if (qt < 0) return;
+  const int m0 = qt * kBM;
+  const int off = kv - qo;  // row i sits at key position i + off
+
+  // keys this tile can see: [0, kv_end)
+  int kv_end = kv;
+  if (causal) kv_end = min(kv, m0 + kBM + off);
+  const int n_kt = kv_end > 0 ? (kv_end + C::BN - 1) / C::BN : 0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int qcol = lane & 31;   // query column of this lane
+  const int half = lane >> 5;   // 0/1
+  const int row = m0 + w * 32 + qcol;     // query row within the request
+  const bool row_ok = row < qo;
+
+  // Q^T operand: lane holds Q[row][ks*16 + 8*half .. +8]
+  bf16x8 qreg[C::KS];
+  {
+    const int r = row_ok ? row : (qo - 1);
+    const uint16_t* qp = q + ((size_t)(q0 + r) * Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = as_bf16x8(load16(qp + ks * 16));
+  }
+
+  f32x16 o[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const int lim = causal ? row + off : 0x7fffffff;  // last visible key of this row (causal)
+
+  // tile loader state
+  const uint16_t* kbase = k;
+  const uint16_t* vbase = v;
+  RaggedLoader rl{k, v, kv0, Hkv, kh, D};
+  PagedLoader pl{k, v, PAGED ? tables + (size_t)b * max_blocks : nullptr, Hkv, kh, D, BS, NB};
+
+  u32x4 kpre[C::UPT], vpre[C::UPT];
+  auto fetch = [&](int n0) {
+#pragma unroll
+    for (int i = 0; i < C::UPT; ++i) {
+      const int u = i * kPrefillThreads + tid;
+      const int rr = u / C::UPR;
+      const int cu = u - rr * C::UPR;
+      const int n = min(n0 + rr, kv - 1);
+      size_t ro;
+      if constexpr (PAGED) ro = pl.row_offset(n); else ro = rl.row_offset(n);
+      kpre[i] = load16(kbase + ro + cu * 8);
+      vpre[i] = load16(vbase + ro + cu * 8);
+    }
+  };
+  auto stash = [&](int n0) {
+#pragma unroll
+    for (int i = 0; i < C::UPT; ++i) {
+      const int u = i * kPrefillThreads + tid;
+      const int rr = u / C::UPR;
+      const int cu = u - rr * C::UPR;
+      u32x4 vv = vpre[i];
+      if (n0 + rr >= kv) vv = u32x4{0, 0, 0, 0};  // rows past the end never carry NaN into PV
+      *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[i];
+      *reinterpret_cast<u32x4*>(v_lds + rr * C::RSE + cu * 8) = vv;
+    }
+  };
+
+  if (n_kt > 0) fetch(0);
+  for (int t = 0; t < n_kt; ++t) {
+    const int n0 = t * C::BN;
+    __syncthreads();  // previous tile fully consumed
+    stash(n0);
+    __syncthreads();
+    if (t + 1 < n_kt) fetch(n0 + C::BN);
+
+    // S^T tile: keys n0 + mt*32 + (8*(r/4) + 4*half + r%4), query qcol
+    f32x16 s[C::MT];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            k_lds + (mt * 32 + qcol) * C::RSE + ks * 16 + 8 * half));
+        s[mt] = mfma32(a, qreg[ks], s[mt]);
+      }
+    }
+
+    // scale + mask (only tiles crossing the ragged end or the causal diagonal)
+    const bool need_mask = (n0 + C::BN > kv) || (causal && n0 + C::BN - 1 > m0 + w * 32 + off);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[mt][r] * scale_log2;
+        if (need_mask) {
+          const int key = n0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key >= kv || key > lim) x = -INFINITY;
+        }
+        s[mt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    // a row that has seen no key yet keeps m = -inf; use 0 as the shift so exp2 gives 0, not NaN
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float corr = fast_exp2(m_run - m_use);
+    float ps = 0.f;
+    bf16x8 pb[C::PS];
+#pragma unroll
+    for (int st = 0; st < C::PS; ++st) {
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float e = fast_exp2(s[st >> 1][8 * (st & 1) + j] - m_use);
+        pv[j] = e;
+        ps += e;
+      }
+      pb[st] = pack_bf16x8(pv);
+    }
+    l_run = l_run * corr + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) o[dt] *= corr;
+
+    // O^T += V^T P^T; k-index 8*half + j <-> key 16*st + 8*(j/4) + 4*half + j%4
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int d = dt * 32 + qcol;
+#pragma unroll
+      for (int st = 0; st < C::PS; ++st) {
+        u32x4 a;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j0 = 2 * jj, j1 = 2 * jj + 1;
+          const int r0 = 16 * st + 8 * (j0 >> 2) + 4 * half + (j0 & 3);
+          const int r1 = 16 * st + 8 * (j1 >> 2) + 4 * half + (j1 & 3);
+          const uint32_t lo = v_lds[r0 * C::RSE + d];
+          const uint32_t hi = v_lds[r1 * C::RSE + d];
+          a[jj] = lo | (hi << 16);
+        }
+        o[dt] = mfma32(as_bf16x8(a), pb[st], o[dt]);
+      }
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  uint16_t* op = out + ((size_t)(q0 + row) * Hq + h) * D;
+  // lane holds d = dt*32 + 8*(r/4) + 4*half + r%4: four runs of 4 consecutive d per d tile
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = dt * 32 + 8 * g + 4 * half;
+      *reinterpret_cast<u32x2*>(op + d) =
+          u32x2{pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
+    }
+}
+
+template <int D, bool PAGED>
+static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
+  const int n_qt = (a.max_qo_len + kBM - 1) / kBM;
+  if (n_qt == 0) return hipSuccess;
+  const int xcd_heads = (a.num_q_heads % 8 == 0) ? a.num_q_heads / 8 : 0;
+  const dim3 grid(a.num_q_heads, a.batch, n_qt);
+  hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(kPrefillThreads), 0, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
+                     a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
+                     a.max_blocks_per_seq, a.causal, a.scale * kLog2e, xcd_heads);
+  return hipGetLastError();
+}
+
+template <bool PAGED>
+static hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return launch_prefill_d<64, PAGED>(a, stream);
+    case 128: return launch_prefill_d<128, PAGED>(a, stream);
+    case 256: return launch_prefill_d<256, PAGED>(a, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+hipError_t launch_ragged_prefill(const PrefillArgs& a, hipStream_t stream) {
+  return launch_prefill<false>(a, stream);
+}
+
+hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream) {
+  return launch_prefill<true>(a, stream);
+}
 
 }  // namespace pkv
