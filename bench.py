@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X (gfx950).
+
+One step runs every call of the hot path once, on inputs already resident in HBM:
+  1. reshape_and_cache + paged_prefill   chunked prefill over a paged prefix: 16 requests, prefix
+                                          U[0,4096], chunk U[64,1024], 16 q / 4 kv heads, head_dim 256
+  2. ragged_prefill                       8 requests, lengths U[128,2048], 32 q / 8 kv heads, hd 128, causal
+  3. paged_attn_decode (library choice)   batch 64, lengths U[512,8192], 32 q / 8 kv heads, hd 128
+  4. paged_attn_decode (split 512)        batch 4, 131072 tokens each, 64 q / 8 kv heads, hd 128
+Each call is bracketed by HIP events on the stream it is launched on. The headline value is the
+decode KV bandwidth (algorithmic bytes of calls 3 and 4 over their measured time); the ragged
+prefill TFLOP/s is reported beside it. The direct decode path of workload 3 is timed separately.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --calibrate-copy     (times a plain 1 GiB device copy, for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import paged_kv_cache_232_amd as pkv  # noqa: E402
+from workloads import CONFIGS, make_config  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0                          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # dense bf16 MFMA, 2516.6 TFLOP/s
+METRIC = "decode KV GB/s (% HBM peak); ragged-prefill bf16 TFLOP/s (% MFMA peak)"
+
+
+# ----------------------------------------------------------------------------------------------
+# Algorithmic work (what the method must move or compute; no padding, no masked work)
+# ----------------------------------------------------------------------------------------------
+def decode_bytes(lens, hq, hkv, d, bs) -> int:
+    """K and V rows of every token + q in + out + the table entries read + seq_lens."""
+    kv = sum(2 * L * hkv * d * 2 for L in lens)
+    qo = 2 * len(lens) * hq * d * 2
+    table = sum((L + bs - 1) // bs for L in lens) * 4 + 4 * len(lens)
+    return kv + qo + table
+
+
+def decode_flops(lens, hq, d) -> int:
+    return sum(4 * L * hq * d for L in lens)
+
+
+def prefill_pairs(qo, kv, causal) -> int:
+    if not causal:
+        return qo * kv
+    off = kv - qo
+    # row i sees keys 0..min(kv-1, i+off)
+    total = 0
+    for i in range(qo):
+        total += max(0, min(kv, i + off + 1))
+    return total
+
+
+def prefill_flops(qo_lens, kv_lens, hq, d, causal) -> int:
+    return sum(4 * d * hq * prefill_pairs(q, k, causal) for q, k in zip(qo_lens, kv_lens))
+
+
+def scatter_bytes(T, hkv, d) -> int:
+    return 2 * (2 * T * hkv * d * 2) + 8 * T  # read k,v + write k,v rows + slots
+
+
+# ----------------------------------------------------------------------------------------------
+class Case:
+    def __init__(self, name, fn, kind, work, unit):
+        self.name, self.fn, self.kind, self.work, self.unit = name, fn, kind, work, unit
+        self.ms = []
+
+    def rate(self, ms):
+        return self.work / (ms * 1e-3) / (1e9 if self.kind == "hbm" else 1e12)
+
+
+def build_cases(dev):
+    cases = {}
+    # workload 5: scatter + paged prefill
+    ci = make_config(5)
+    spec = CONFIGS[5]
+    c5 = dict(q=ci.q.to(dev), k_new=ci.k_new.to(dev), v_new=ci.v_new.to(dev), kc=ci.k_cache.to(dev),
+              vc=ci.v_cache.to(dev), bt=ci.block_tables.to(dev), slots=ci.slot_mapping.to(dev),
+              qi=ci.qo_indptr.to(dev), kl=ci.kv_lens.to(dev), qi_h=ci.qo_indptr, kl_h=ci.kv_lens,
+              scale=ci.scale)
+    c5["out"] = torch.empty_like(c5["q"])
+    T5 = int(ci.qo_indptr[-1])
+    chunk = [int(ci.qo_indptr[b + 1] - ci.qo_indptr[b]) for b in range(len(ci.kv_lens))]
+    kvl5 = ci.kv_lens.tolist()
+    cases["scatter5"] = Case(
+        "reshape_and_cache (chunked prefill, 16 req, hd 256)",
+        lambda: pkv.reshape_and_cache(c5["k_new"], c5["v_new"], c5["kc"], c5["vc"], c5["slots"]),
+        "hbm", scatter_bytes(T5, spec["num_kv_heads"], spec["head_dim"]), "GB/s")
+    cases["paged5"] = Case(
+        "paged_prefill (16 req, prefix U[0,4096], chunk U[64,1024], 16/4 heads, hd 256)",
+        lambda: pkv.paged_prefill(c5["q"], c5["kc"], c5["vc"], c5["bt"], c5["qi"], c5["kl"], True, c5["scale"],
+                                  qo_indptr_h=c5["qi_h"], kv_lens_h=c5["kl_h"], out=c5["out"]),
+        "mfma", prefill_flops(chunk, kvl5, spec["num_q_heads"], spec["head_dim"], True), "TFLOP/s")
+    meta = {"T5": T5, "prefix_mean": float(ci.prefix_lens.float().mean()), "chunk_mean": T5 / len(chunk)}
+    del ci
+
+    # workload 2: ragged prefill
+    ri = make_config(2)
+    spec = CONFIGS[2]
+    c2 = dict(q=ri.q.to(dev), k=ri.k.to(dev), v=ri.v.to(dev), qi=ri.qo_indptr.to(dev), ki=ri.kv_indptr.to(dev),
+              qi_h=ri.qo_indptr, ki_h=ri.kv_indptr, scale=ri.scale)
+    c2["out"] = torch.empty_like(c2["q"])
+    lens2 = [int(ri.qo_indptr[b + 1] - ri.qo_indptr[b]) for b in range(8)]
+    cases["ragged2"] = Case(
+        "ragged_prefill (8 req, U[128,2048], 32/8 heads, hd 128, causal)",
+        lambda: pkv.ragged_prefill(c2["q"], c2["k"], c2["v"], c2["qi"], c2["ki"], True, c2["scale"],
+                                   qo_indptr_h=c2["qi_h"], kv_indptr_h=c2["ki_h"], out=c2["out"]),
+        "mfma", prefill_flops(lens2, lens2, spec["num_q_heads"], spec["head_dim"], True), "TFLOP/s")
+    meta["lens2"] = lens2
+    del ri
+
+    # workloads 3 and 4: decode
+    for cid, key in ((3, "decode3"), (4, "decode4")):
+        di = make_config(cid)
+        spec = CONFIGS[cid]
+        c = dict(q=di.q.to(dev), kc=di.k_cache.to(dev), vc=di.v_cache.to(dev), bt=di.block_tables.to(dev),
+                 sl=di.seq_lens.to(dev), msl=di.max_seq_len, scale=di.scale)
+        c["out"] = torch.empty_like(c["q"])
+        B, Hq, D = di.q.shape
+        Hkv = spec["num_kv_heads"]
+        lens = di.seq_lens.tolist()
+        pt = -1 if cid == 3 else 512
+        need = pkv.decode_workspace_bytes(B, Hq, Hkv, D, di.max_seq_len, 512)
+        c["ws"] = torch.empty(need, dtype=torch.uint8, device=dev)
+        work = decode_bytes(lens, Hq, Hkv, D, di.block_size)
+
+        def mk(c=c, pt=pt):
+            return lambda: pkv.paged_attn_decode(c["q"], c["kc"], c["vc"], c["bt"], c["sl"], c["scale"],
+                                                 max_seq_len=c["msl"], partition_tokens=pt, out=c["out"],
+                                                 workspace=c["ws"])
+        cases[key] = Case(f"paged_attn_decode ({CONFIGS[cid]['name']}, B={B}, {Hq}/{Hkv} heads, hd {D})",
+                          mk(), "hbm", work, "GB/s")
+        if cid == 3:
+            cases["decode3_direct"] = Case("paged_attn_decode direct path (batched decode)", mk(c, 0), "hbm", work,
+                                           "GB/s")
+            cases["decode3_split"] = Case("paged_attn_decode split 512 (batched decode)", mk(c, 512), "hbm", work,
+                                          "GB/s")
+        meta[f"lens{cid}_sum"] = sum(lens)
+        meta[f"flops{cid}"] = decode_flops(lens, Hq, D)
+        del di
+    return cases, meta
+
+
+STEP = ["scatter5", "paged5", "ragged2", "decode3", "decode4"]
+
+
+def time_step(cases, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for k in STEP:
+            cases[k].fn()
+    torch.cuda.synchronize()
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+          for k in STEP}
+    whole0 = torch.cuda.Event(enable_timing=True)
+    whole1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    whole0.record(stream)
+    for s in range(steps):
+        for k in STEP:
+            ev[k][s][0].record(stream)
+            cases[k].fn()
+            ev[k][s][1].record(stream)
+    whole1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for k in STEP:
+        cases[k].ms = [a.elapsed_time(b) for a, b in ev[k]]
+    return whole0.elapsed_time(whole1) / steps, wall
+
+
+def time_alone(case, reps=20, warmup=5):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        case.fn()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        a.record(stream)
+        case.fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    case.ms = [a.elapsed_time(b) for a, b in pairs]
+
+
+# ----------------------------------------------------------------------------------------------
+def cpu_baseline(meta):
+    """The fp64 oracle on the host cores, on a bounded sample of the decode workload."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    import oracle
+    di = make_config(3)
+    spec = CONFIGS[3]
+    n = 8  # first 8 of the 64 sequences
+    lens = di.seq_lens[:n].tolist()
+    t0 = time.perf_counter()
+    oracle.paged_decode(di.q[:n], di.k_cache, di.v_cache, di.block_tables[:n], di.seq_lens[:n], di.scale)
+    dt = time.perf_counter() - t0
+    work = decode_bytes(lens, spec["num_q_heads"], spec["num_kv_heads"], spec["head_dim"], di.block_size)
+    gbs = work / dt / 1e9
+    # prefill sample: the shortest request of the ragged workload
+    ri = make_config(2)
+    lens2 = meta["lens2"]
+    b = int(np.argmin(lens2))
+    q0, q1 = int(ri.qo_indptr[b]), int(ri.qo_indptr[b + 1])
+    import torch as _t
+    qi = _t.tensor([0, q1 - q0], dtype=_t.int32)
+    t1 = time.perf_counter()
+    oracle.ragged_prefill(ri.q[q0:q1], ri.k[q0:q1], ri.v[q0:q1], qi, qi, True, ri.scale)
+    dt2 = time.perf_counter() - t1
+    fl = prefill_flops([q1 - q0], [q1 - q0], 32, 128, True)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"batched decode workload, first {n} of 64 sequences ({sum(lens)} tokens), fp64 NumPy, "
+                      f"{dt:.2f} s",
+            "prefill": {"value": round(fl / dt2 / 1e12, 6), "unit": "TFLOP/s",
+                        "sample": f"ragged prefill workload, request {b} ({q1 - q0} rows) alone, {dt2:.2f} s"}}
+
+
+def calibrate_copy(dev):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 5
+    print(json.dumps({"copy_bytes_each_way": n, "ms": ms, "GB/s_read_plus_write": 2 * n / ms / 1e6}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library's hot path runs on a single MI355X and no "
+              "multi-GPU path is built (see the sharding notes in the design document).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pkv.load_library()
+    if args.calibrate_copy:
+        calibrate_copy(dev)
+        return
+    print(f"# device: {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+    cases, meta = build_cases(dev)
+    print("# inputs resident; timing", file=sys.stderr, flush=True)
+    ms_step, wall = time_step(cases, args.steps, args.warmup)
+    for k in ("decode3_direct", "decode3_split"):
+        time_alone(cases[k])
+
+    def summary(k):
+        c = cases[k]
+        avg = statistics.fmean(c.ms)
+        med = statistics.median(c.ms)
+        peak = HBM_PEAK_GBS if c.kind == "hbm" else MFMA_BF16_PEAK_TFLOPS
+        r = c.rate(avg)
+        return {"call": c.name, "avg_ms": round(avg, 5), "median_ms": round(med, 5), "work": c.work,
+                "rate": round(r, 2), "unit": c.unit, "frac_of_peak": round(r / peak, 4)}
+
+    per = {k: summary(k) for k in STEP + ["decode3_direct", "decode3_split"]}
+    dec_ms = sum(statistics.fmean(cases[k].ms) for k in ("decode3", "decode4"))
+    dec_bytes = cases["decode3"].work + cases["decode4"].work
+    value = dec_bytes / (dec_ms * 1e-3) / 1e9
+    pre = per["ragged2"]
+    # dominant call of the step (largest share of the step time)
+    dom = max(STEP, key=lambda k: statistics.fmean(cases[k].ms))
+    dc = cases[dom]
+    dpeak = HBM_PEAK_GBS if dc.kind == "hbm" else MFMA_BF16_PEAK_TFLOPS
+    dach = dc.rate(statistics.fmean(dc.ms))
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, shuffled block pools; no dataset)",
+        "config": {
+            "workload": "paged-KV attention hot path per step: scatter + chunked paged prefill (16 req, "
+                        "prefix U[0,4096], chunk U[64,1024], 16/4 heads, hd 256); ragged causal prefill (8 req, "
+                        "U[128,2048], 32/8 heads, hd 128); batched paged decode (B=64, U[512,8192], 32/8 heads, "
+                        "hd 128); long-context split decode (B=4, 131072, 64/8 heads, hd 128)",
+            "global_batch": 64 + 4,
+            "block_size": 16,
+            "partition_tokens": 512,
+            "parallelism": "none (1 GPU)",
+        },
+        "decode_hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "prefill": {"value": pre["rate"], "unit": "TFLOP/s", "frac": pre["frac_of_peak"],
+                    "workload": "ragged causal prefill, 8 requests U[128,2048], 32/8 heads, hd 128"},
+        "roofline": {"bound": "hbm" if dc.kind == "hbm" else "mfma", "kernel": dc.name,
+                     "achieved": round(dach, 2), "peak": dpeak,
+                     "unit": "GB/s" if dc.kind == "hbm" else "TFLOP/s", "frac": round(dach / dpeak, 4),
+                     "traffic": None},
+        "per_call": per,
+        "wall_s_timed": round(wall, 4),
+    }
+    line["cpu_baseline"] = cpu_baseline(meta)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
