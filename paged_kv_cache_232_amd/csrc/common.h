@@ -35,15 +35,15 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950; NaN stays NaN).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
@@ -53,6 +53,16 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
   r[2] = pack_bf16x2(v[4], v[5]);
   r[3] = pack_bf16x2(v[6], v[7]);
   return as_bf16x8(r);
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group, lanes 4r..4r+3
+// each supply the address of 4 consecutive 16-bit elements; together they form row r (16
+// elements) of a 4 x 16 block, and lane i of the group receives column i: the 4 values
+// (row0[i], row1[i], row2[i], row3[i]).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {

@@ -29,6 +29,9 @@ namespace pkv {
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 constexpr int kBM = 32 * kPrefillWaves;  // query rows per work-group
+// A row's running max is only raised (and O, l rescaled) when a tile's max exceeds it by more than
+// this many log2 units; otherwise probabilities are taken against the stale max and stay <= 2^8.
+constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
 struct PrefillCfg {
@@ -41,13 +44,12 @@ struct PrefillCfg {
   static constexpr int UPR = D / 8;                 // 16-byte units per row
   static constexpr int UNITS = BN * UPR;            // units per tile (K or V)
   static constexpr int UPT = UNITS / kPrefillThreads;  // units per thread
+  static constexpr int LDS_ROWS = (2 * BN > kBM) ? 2 * BN : kBM;  // K+V tiles, or the output tile
   static_assert(UNITS % kPrefillThreads == 0, "tile units must divide evenly");
 };
 
 struct RaggedLoader {
-  const uint16_t* k;
-  const uint16_t* v;
-  int64_t row0;   // first kv row of the request
+  int64_t row0;  // first kv row of the request
   int Hkv, kh, D;
   __device__ __forceinline__ size_t row_offset(int n) const {
     return ((size_t)(row0 + n) * Hkv + kh) * D;
@@ -55,8 +57,6 @@ struct RaggedLoader {
 };
 
 struct PagedLoader {
-  const uint16_t* k;
-  const uint16_t* v;
   const int32_t* trow;  // this request's block-table row
   int Hkv, kh, D, BS, NB;
   __device__ __forceinline__ size_t row_offset(int n) const {
@@ -65,6 +65,8 @@ struct PagedLoader {
   }
 };
 
+// scale_log2 > 0 always: the host folds a negative scale into negate_q (an exact sign flip of q)
+// and replaces a zero scale by the smallest normal float (every score then rounds to 2^0 = 1).
 template <int D, bool PAGED>
 __global__ void __launch_bounds__(kPrefillThreads)
 prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -72,10 +74,11 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
                const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ tables,
                int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
-               int xcd_heads) {
+               int negate_q, int xcd_heads) {
   using C = PrefillCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::BN * C::RSE];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[C::BN * C::RSE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ROWS * C::RSE];
+  uint16_t* const k_lds = smem;
+  uint16_t* const v_lds = smem + C::BN * C::RSE;
 
   // block x -> q head: heads sharing a kv head go to the same XCD (round-robin x % 8)
   int h = blockIdx.x;
@@ -118,8 +121,13 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   {
     const int r = row_ok ? row : (qo - 1);
     const uint16_t* qp = q + ((size_t)(q0 + r) * Hq + h) * D + 8 * half;
+    const uint32_t flip = negate_q ? 0x80008000u : 0u;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = as_bf16x8(load16(qp + ks * 16));
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 x = load16(qp + ks * 16);
+      x ^= u32x4{flip, flip, flip, flip};
+      qreg[ks] = as_bf16x8(x);
+    }
   }
 
   f32x16 o[C::DT];
@@ -127,15 +135,13 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;  // log2 units
   float l_run = 0.f;
-  const int lim = causal ? row + off : 0x7fffffff;  // last visible key of this row (causal)
+  // last visible key of this row: the causal limit and the ragged end in one bound
+  const int lim = causal ? min(row + off, kv - 1) : kv - 1;
 
-  // tile loader state
-  const uint16_t* kbase = k;
-  const uint16_t* vbase = v;
-  RaggedLoader rl{k, v, kv0, Hkv, kh, D};
-  PagedLoader pl{k, v, PAGED ? tables + (size_t)b * max_blocks : nullptr, Hkv, kh, D, BS, NB};
+  const RaggedLoader rl{kv0, Hkv, kh, D};
+  const PagedLoader pl{PAGED ? tables + (size_t)b * max_blocks : nullptr, Hkv, kh, D, BS, NB};
 
   u32x4 kpre[C::UPT], vpre[C::UPT];
   auto fetch = [&](int n0) {
@@ -147,8 +153,8 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const int n = min(n0 + rr, kv - 1);
       size_t ro;
       if constexpr (PAGED) ro = pl.row_offset(n); else ro = rl.row_offset(n);
-      kpre[i] = load16(kbase + ro + cu * 8);
-      vpre[i] = load16(vbase + ro + cu * 8);
+      kpre[i] = load16(k + ro + cu * 8);
+      vpre[i] = load16(v + ro + cu * 8);
     }
   };
   auto stash = [&](int n0) {
@@ -164,6 +170,12 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   };
 
+  // Transpose-read addresses of the V^T operand: 16-lane group g reads key rows
+  // 4*(g/2) + (l%16)/4 (+8 for the second read) at columns 16*(g%2) + 4*(l%4) of each d tile.
+  const int grp = lane >> 4;
+  const int tr_row = 4 * (grp >> 1) + ((lane & 15) >> 2);
+  const int tr_col = 16 * (grp & 1) + 4 * (lane & 3);
+
   if (n_kt > 0) fetch(0);
   for (int t = 0; t < n_kt; ++t) {
     const int n0 = t * C::BN;
@@ -172,40 +184,48 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __syncthreads();
     if (t + 1 < n_kt) fetch(n0 + C::BN);
 
-    // S^T tile: keys n0 + mt*32 + (8*(r/4) + 4*half + r%4), query qcol
+    // S^T tile: lane holds keys n0 + mt*32 + 8*(r/4) + 4*half + r%4 of query qcol (raw scores)
     f32x16 s[C::MT];
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
+    for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
             k_lds + (mt * 32 + qcol) * C::RSE + ks * 16 + 8 * half));
         s[mt] = mfma32(a, qreg[ks], s[mt]);
       }
-    }
 
-    // scale + mask (only tiles crossing the ragged end or the causal diagonal)
+    // mask only tiles crossing the ragged end or this wave's causal diagonal
     const bool need_mask = (n0 + C::BN > kv) || (causal && n0 + C::BN - 1 > m0 + w * 32 + off);
+    if (need_mask) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = n0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key > lim) s[mt][r] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[mt][r] * scale_log2;
-        if (need_mask) {
-          const int key = n0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= kv || key > lim) x = -INFINITY;
-        }
-        s[mt][r] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    // a row that has seen no key yet keeps m = -inf; use 0 as the shift so exp2 gives 0, not NaN
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float corr = fast_exp2(m_run - m_use);
+    const float tmax = mx * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleLog2) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= corr;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) o[dt] *= corr;
+    }
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
     float ps = 0.f;
     bf16x8 pb[C::PS];
 #pragma unroll
@@ -213,52 +233,50 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       float pv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float e = fast_exp2(s[st >> 1][8 * (st & 1) + j] - m_use);
+        const float e = fast_exp2(__builtin_fmaf(s[st >> 1][8 * (st & 1) + j], scale_log2, neg_m));
         pv[j] = e;
         ps += e;
       }
       pb[st] = pack_bf16x8(pv);
     }
-    l_run = l_run * corr + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) o[dt] *= corr;
+    l_run += ps;
 
     // O^T += V^T P^T; k-index 8*half + j <-> key 16*st + 8*(j/4) + 4*half + j%4
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const int d = dt * 32 + qcol;
+    for (int st = 0; st < C::PS; ++st)
 #pragma unroll
-      for (int st = 0; st < C::PS; ++st) {
-        u32x4 a;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int j0 = 2 * jj, j1 = 2 * jj + 1;
-          const int r0 = 16 * st + 8 * (j0 >> 2) + 4 * half + (j0 & 3);
-          const int r1 = 16 * st + 8 * (j1 >> 2) + 4 * half + (j1 & 3);
-          const uint32_t lo = v_lds[r0 * C::RSE + d];
-          const uint32_t hi = v_lds[r1 * C::RSE + d];
-          a[jj] = lo | (hi << 16);
-        }
-        o[dt] = mfma32(as_bf16x8(a), pb[st], o[dt]);
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const uint16_t* vp = v_lds + (16 * st + tr_row) * C::RSE + dt * 32 + tr_col;
+        const u32x2 lo = lds_read_tr16(vp);
+        const u32x2 hi = lds_read_tr16(vp + 8 * C::RSE);
+        o[dt] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[st], o[dt]);
       }
-    }
   }
 
+  // normalise, stage the wave's 32 rows in LDS, then write whole rows with 16-byte stores
   l_run += __shfl_xor(l_run, 32);
-  if (!row_ok) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  uint16_t* op = out + ((size_t)(q0 + row) * Hq + h) * D;
-  // lane holds d = dt*32 + 8*(r/4) + 4*half + r%4: four runs of 4 consecutive d per d tile
+  __syncthreads();
+  uint16_t* const ost = smem + w * 32 * C::RSE;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = dt * 32 + 8 * g + 4 * half;
-      *reinterpret_cast<u32x2*>(op + d) =
+      *reinterpret_cast<u32x2*>(ost + qcol * C::RSE + d) =
           u32x2{pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
                 pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
     }
+  __syncthreads();
+#pragma unroll
+  for (int u = lane; u < 32 * C::UPR; u += kWave) {
+    const int rr = u / C::UPR;
+    const int cu = u - rr * C::UPR;
+    const int orow = m0 + w * 32 + rr;
+    if (orow < qo)
+      store16(out + ((size_t)(q0 + orow) * Hq + h) * D + cu * 8,
+              *reinterpret_cast<const u32x4*>(ost + rr * C::RSE + cu * 8));
+  }
 }
 
 template <int D, bool PAGED>
@@ -266,12 +284,16 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
   const int n_qt = (a.max_qo_len + kBM - 1) / kBM;
   if (n_qt == 0) return hipSuccess;
   const int xcd_heads = (a.num_q_heads % 8 == 0) ? a.num_q_heads / 8 : 0;
+  float scale_log2 = a.scale * kLog2e;
+  const int negate_q = scale_log2 < 0.f;
+  if (negate_q) scale_log2 = -scale_log2;
+  if (!(scale_log2 >= 1.17549435e-38f)) scale_log2 = 1.17549435e-38f;  // zero (or denormal) scale
   const dim3 grid(a.num_q_heads, a.batch, n_qt);
   hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(kPrefillThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
                      a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
-                     a.max_blocks_per_seq, a.causal, a.scale * kLog2e, xcd_heads);
+                     a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads);
   return hipGetLastError();
 }
 
