@@ -20,8 +20,8 @@
  *   - Slots that hold no token (the tail of a sequence's last block, unused blocks) may hold any
  *     bits, NaN included: they are excluded by length, never read into a result.
  *
- * Supported: head_dim in {64, 128, 256}; num_q_heads % num_kv_heads == 0; block_size a multiple
- * of 16 up to 256; bf16 data, fp32 accumulation, bf16 output rounded to nearest even.
+ * Supported: head_dim in {64, 128, 256}; num_q_heads % num_kv_heads == 0; block_size a power of
+ * two from 16 to 256; bf16 data, fp32 accumulation, bf16 output rounded to nearest even.
  */
 #ifndef PKV_H
 #define PKV_H

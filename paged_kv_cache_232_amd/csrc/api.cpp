@@ -13,7 +13,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 
-bool block_size_ok(int bs) { return bs >= 16 && bs <= 256 && bs % 16 == 0; }
+bool block_size_ok(int bs) { return bs >= 16 && bs <= 256 && (bs & (bs - 1)) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_E_HIP; }
 

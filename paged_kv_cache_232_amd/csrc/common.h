@@ -71,6 +71,40 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions across lanes l and l ^ 16 (resp. l ^ 32) with gfx950's v_permlane16_swap /
+// v_permlane32_swap: with both operands holding x, the two results hold x of rows {0,2} and of
+// rows {1,3} (resp. of the low and high half), so combining them reduces over the partner lanes in
+// VALU only. The second operand is passed through an empty asm so the compiler cannot treat the
+// two operands as one value (it otherwise folds the swap of identical operands away).
+__device__ __forceinline__ uint2 swap16(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("" : "+v"(b));
+  const auto p = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  return uint2{p[0], p[1]};
+}
+__device__ __forceinline__ uint2 swap32(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("" : "+v"(b));
+  const auto p = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return uint2{p[0], p[1]};
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const uint2 p = swap16(x);
+  return fmaxf(__builtin_bit_cast(float, p.x), __builtin_bit_cast(float, p.y));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const uint2 p = swap32(x);
+  return fmaxf(__builtin_bit_cast(float, p.x), __builtin_bit_cast(float, p.y));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const uint2 p = swap16(x);
+  return __builtin_bit_cast(float, p.x) + __builtin_bit_cast(float, p.y);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const uint2 p = swap32(x);
+  return __builtin_bit_cast(float, p.x) + __builtin_bit_cast(float, p.y);
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -81,5 +115,35 @@ template <typename T>
 __device__ __forceinline__ T clampi(T x, T lo, T hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
+
+// A wave's sliding view of one block-table row: 64 consecutive entries held one per lane, with the
+// next 64 already loaded. Block ids come out with v_readlane (a scalar), so forming a page address
+// never waits on a table load issued behind in-flight data loads. Indices passed to get() must be
+// wave-uniform and non-decreasing. Entries past the row width read as 0.
+struct TableWindow {
+  const int32_t* row;
+  int width;
+  int base;
+  int cur;
+  int nxt;
+
+  __device__ __forceinline__ void init(const int32_t* r, int w, int first_index, int lane) {
+    row = r;
+    width = w;
+    base = first_index & ~63;
+    const int j0 = base + lane, j1 = base + 64 + lane;
+    cur = j0 < width ? row[j0] : 0;
+    nxt = j1 < width ? row[j1] : 0;
+  }
+  __device__ __forceinline__ int get(int index, int lane) {
+    while (index >= base + 64) {
+      base += 64;
+      cur = nxt;
+      const int j = base + 64 + lane;
+      nxt = j < width ? row[j] : 0;
+    }
+    return __builtin_amdgcn_readlane(cur, index - base);
+  }
+};
 
 }  // namespace pkv

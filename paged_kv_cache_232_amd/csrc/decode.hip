@@ -24,17 +24,24 @@
 
 namespace pkv {
 
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodeThreads = kDecodeWaves * kWave;
+constexpr int kDirectWaves = 4;  // waves per work-group on the direct path (one per split partition)
+constexpr float kRescaleLog2 = 8.0f;  // raise a running max only when exceeded by more than this
+constexpr int kPrefetch = 2;          // 32-token chunks per wave in flight (loads issued ahead)
 
 template <int D>
 struct DecodeCfg {
   static constexpr int KK = D / 32;           // 32-wide d slices of the QK MFMA
   static constexpr int MT = D / 16;           // 16-row d tiles of the PV MFMA
   static constexpr int VU = D / 32;           // 16-byte V units per lane per half page
-  static constexpr int RS = 2 * D + 8;        // LDS bytes per staged V row (8-byte pad)
+  static constexpr int RS = 2 * D + 32;       // LDS bytes per staged V row (pad: conflict-free tr reads)
   static constexpr int WAVE_LDS = 32 * RS;    // one wave's 32-row V tile
   static_assert(WAVE_LDS >= D * 16 * 4, "combine buffer must fit in a wave's V tile");
+};
+
+template <int D>
+struct DecodeChunk {
+  u32x4 k[2][DecodeCfg<D>::KK];
+  u32x4 v[2][DecodeCfg<D>::VU];
 };
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -46,25 +53,28 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <int D, bool SPLIT>
-__global__ void __launch_bounds__(kDecodeThreads)
+// scale_log2 > 0 always: the host folds a negative scale into negate_q (an exact sign flip of q)
+// and replaces a zero scale by the smallest normal float (every probability is then exactly 1).
+template <int D, int NW, bool SPLIT>
+__global__ void __launch_bounds__(NW * kWave, D <= 128 ? 2 : 1)
 decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
               const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables,
               const int32_t* __restrict__ lens, uint16_t* __restrict__ out,
               float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ m_part,
               float* __restrict__ l_part, int Hq, int Hkv, int G, int n_hg, int BS, int NB,
-              int max_blocks, int PT, int Pmax, float scale_log2) {
+              int max_blocks, int PT, int Pmax, float scale_log2, int negate_q, int bs_shift) {
   using C = DecodeCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[kDecodeWaves * C::WAVE_LDS];
-  __shared__ float sm_m[kDecodeWaves][16];
-  __shared__ float sm_l[kDecodeWaves][16];
+  using Chunk = DecodeChunk<D>;
+  __shared__ __attribute__((aligned(16))) char smem[NW * C::WAVE_LDS];
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
 
   const int p = blockIdx.x;
   const int kh = blockIdx.y / n_hg;
   const int hg = blockIdx.y - kh * n_hg;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept scalar
   const int col = lane & 15;  // head column of the MFMA tiles
   const int qg = lane >> 4;   // lane group 0..3
 
@@ -85,9 +95,11 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
   bf16x8 qreg[C::KK];
   {
     const uint16_t* qp = q + ((size_t)b * Hq + hq) * D + 8 * qg;
+    const uint32_t flip = negate_q ? 0x80008000u : 0u;
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
       u32x4 v = load16(qp + kk * 32);
+      v ^= u32x4{flip, flip, flip, flip};
       if (!col_ok) v = u32x4{0, 0, 0, 0};
       qreg[kk] = as_bf16x8(v);
     }
@@ -96,7 +108,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
   f32x4 o[C::MT];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;  // log2 units
   float l_run = 0.f;
 
   char* vbuf = smem + w * C::WAVE_LDS;
@@ -105,165 +117,227 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
   const int32_t* trow = tables + (size_t)b * max_blocks;
   const size_t head_stride = (size_t)BS * D;
   const size_t block_stride = (size_t)Hkv * head_stride;
+  const int last = t_end - 1;
+  // transpose-read address of the V^T operand: group qg reads token rows 4*qg + (l%16)/4
+  // (+16 for the second half page) at columns 4*(l%4) of each 16-wide d tile
+  const int tr_off = (4 * qg + ((lane & 15) >> 2)) * (C::RS / 2) + 4 * (lane & 3);
 
-  for (int c = w; c < n_chunks; c += kDecodeWaves) {
+  TableWindow tw;
+  tw.init(trow, max_blocks, (t_begin + w * 32) >> bs_shift, lane);
+
+  const int koff = col * D + 8 * qg;  // this lane's K element within a 16-row half page
+  const int voff = lane * 8;          // this lane's first V element within a half page
+
+  auto load = [&](Chunk& ch, int c) {
     const int cs = t_begin + c * 32;
-    size_t base[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int tok0 = cs + 16 * hh;
       const int tk = tok0 < t_end ? tok0 : cs;  // an all-masked half page re-reads a valid one
-      const int blk = clampi(trow[tk / BS], 0, NB - 1);
-      base[hh] = (size_t)blk * block_stride + (size_t)kh * head_stride + (size_t)(tk % BS) * D;
+      const int blk = clampi(tw.get(tk >> bs_shift, lane), 0, NB - 1);
+      const size_t base = (size_t)blk * block_stride + (size_t)kh * head_stride +
+                          (size_t)(tk & (BS - 1)) * D;
+      const uint16_t* kp = kc + base;
+      const uint16_t* vp = vc + base;
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) ch.k[hh][kk] = load16(kp + koff + kk * 32);
+#pragma unroll
+      for (int i = 0; i < C::VU; ++i) ch.v[hh][i] = load16(vp + voff + i * 512);
     }
-    u32x4 kr[2][C::KK];
-    u32x4 vr[2][C::VU];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk)
-        kr[hh][kk] = load16(kc + base[hh] + (size_t)col * D + kk * 32 + 8 * qg);
-#pragma unroll
-      for (int i = 0; i < C::VU; ++i) vr[hh][i] = load16(vc + base[hh] + (size_t)(i * 64 + lane) * 8);
-    }
+  };
 
+  auto process = [&](const Chunk& ch, int c) {
+    const int cs = t_begin + c * 32;
+    const bool partial = cs + 31 > last;  // only a partition's last chunk can hold slack rows
     // S^T[token][head] for the two half pages
     f32x4 s[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) s[hh] = mfma16(as_bf16x8(kr[hh][kk]), qreg[kk], s[hh]);
+      for (int kk = 0; kk < C::KK; ++kk) s[hh] = mfma16(as_bf16x8(ch.k[hh][kk]), qreg[kk], s[hh]);
     }
-
     // stage V rows in LDS; rows past the end are zeroed (select, so NaN slack never leaks)
+    if (!partial) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int i = 0; i < C::VU; ++i) {
-        const int u = i * 64 + lane;
-        const int row = u / (D / 8);
-        const int cu = u - row * (D / 8);
-        u32x4 val = vr[hh][i];
-        if (cs + 16 * hh + row >= t_end) val = u32x4{0, 0, 0, 0};
-        char* dst = vbuf + (16 * hh + row) * C::RS + cu * 16;
-        *reinterpret_cast<u32x2*>(dst) = u32x2{val[0], val[1]};
-        *reinterpret_cast<u32x2*>(dst + 8) = u32x2{val[2], val[3]};
-      }
+        for (int i = 0; i < C::VU; ++i) {
+          const int u = i * 64 + lane;
+          const int row = u / (D / 8);
+          *reinterpret_cast<u32x4*>(vbuf + (16 * hh + row) * C::RS + (u - row * (D / 8)) * 16) = ch.v[hh][i];
+        }
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < C::VU; ++i) {
+          const int u = i * 64 + lane;
+          const int row = u / (D / 8);
+          u32x4 val = ch.v[hh][i];
+          if (cs + 16 * hh + row > last) val = u32x4{0, 0, 0, 0};
+          *reinterpret_cast<u32x4*>(vbuf + (16 * hh + row) * C::RS + (u - row * (D / 8)) * 16) = val;
+        }
     }
-
-    // scores in log2 units, masked past the end
+    // raw scores (masked past the end on a partial chunk); running max in log2 units, raised lazily
     float sv[8];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = cs + 16 * hh + 4 * qg + r;
-        const float x = s[hh][r] * scale_log2;
-        sv[hh * 4 + r] = tok < t_end ? x : -INFINITY;
-      }
-    float mx = sv[0];
+      for (int r = 0; r < 4; ++r) sv[hh * 4 + r] = s[hh][r];
+    if (partial) {
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float corr = fast_exp2(m_run - m_new);
+      for (int j = 0; j < 8; ++j)
+        if (cs + 16 * (j >> 2) + 4 * qg + (j & 3) > last) sv[j] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    mx = max_xor32(max_xor16(mx));
+    const float tmax = mx * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleLog2) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= corr;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) o[mt] *= corr;
+    }
+    const float neg_m = -m_run;  // finite: every chunk holds at least one valid token
     float pv[8];
-    float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      pv[j] = fast_exp2(sv[j] - m_new);
-      ps += pv[j];
+      pv[j] = fast_exp2(__builtin_fmaf(sv[j], scale_log2, neg_m));
+      l_run += pv[j];
     }
-    l_run = l_run * corr + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) o[mt] *= corr;
     // B operand of PV: k-index 8*qg + j <-> token 16*(j/4) + 4*qg + j%4, exactly this lane's scores
     const bf16x8 pb = pack_bf16x8(pv);
-
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
-      const int d = mt * 16 + col;
-      u32x4 a;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j0 = 2 * jj, j1 = 2 * jj + 1;
-        const int r0 = 16 * (j0 >> 2) + 4 * qg + (j0 & 3);
-        const int r1 = 16 * (j1 >> 2) + 4 * qg + (j1 & 3);
-        const uint32_t lo = vl[r0 * (C::RS / 2) + d];
-        const uint32_t hi = vl[r1 * (C::RS / 2) + d];
-        a[jj] = lo | (hi << 16);
-      }
-      o[mt] = mfma16(as_bf16x8(a), pb, o[mt]);
+      const uint16_t* vp = vl + tr_off + mt * 16;
+      const u32x2 lo = lds_read_tr16(vp);
+      const u32x2 hi = lds_read_tr16(vp + 16 * (C::RS / 2));
+      o[mt] = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, o[mt]);
     }
     __builtin_amdgcn_wave_barrier();
+  };
+
+  // chunks w, w+NW, ... with the next kPrefetch-1 chunks' loads in flight while one is processed.
+  // The steady-state loop issues its look-ahead loads unconditionally, so the compiler can count
+  // exactly which loads a chunk must wait for; the tail drains in a guarded epilogue.
+  {
+    Chunk ring[kPrefetch];
+    int c = w;
+#pragma unroll
+    for (int i = 0; i < kPrefetch - 1; ++i)
+      if (c + i * NW < n_chunks) load(ring[i], c + i * NW);
+    while (c + (2 * kPrefetch - 2) * NW < n_chunks) {
+#pragma unroll
+      for (int sl = 0; sl < kPrefetch; ++sl) {
+        load(ring[(sl + kPrefetch - 1) % kPrefetch], c + (kPrefetch - 1) * NW);
+        process(ring[sl], c);
+        c += NW;
+      }
+    }
+#pragma unroll
+    for (int sl = 0; sl < 2 * kPrefetch - 1; ++sl) {
+      if (c < n_chunks) {
+        const int ahead = c + (kPrefetch - 1) * NW;
+        if (ahead < n_chunks) load(ring[(sl + kPrefetch - 1) % kPrefetch], ahead);
+        process(ring[sl % kPrefetch], c);
+        c += NW;
+      }
+    }
   }
 
   // lane-group partial sums -> per-column sums (m_run is already uniform per column)
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_xor32(sum_xor16(l_run));
 
-  __syncthreads();  // every wave is done with its V tile; reuse it for O^T [d][16]
-  float* obuf = reinterpret_cast<float*>(vbuf);
+  if constexpr (NW == 1) {
+    // a single wave owns the whole work item: normalise and write straight from registers
+    if (!col_ok) return;
+    const int hout = kh * G + gcol;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    if constexpr (SPLIT) {
+      const size_t pi = ((size_t)b * Hq + hout) * Pmax + p;
+      float* op = o_part + pi * D + 4 * qg;
 #pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt)
+      for (int mt = 0; mt < C::MT; ++mt) *reinterpret_cast<f32x4*>(op + mt * 16) = o[mt] * inv;
+      if (qg == 0) {
+        m_part[pi] = m_run;
+        l_part[pi] = l_run;
+      }
+    } else {
+      uint16_t* op = out + ((size_t)b * Hq + hout) * D + 4 * qg;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) obuf[(mt * 16 + 4 * qg + r) * 16 + col] = o[mt][r];
-  if (lane < 16) {
-    sm_m[w][lane] = m_run;
-    sm_l[w][lane] = l_run;
-  }
-  __syncthreads();
-
-  const int t = threadIdx.x;
-  const int oc = t >> 4;     // head column
-  const int dpart = t & 15;  // this thread's D/16 consecutive outputs
-  if (hg * 16 + oc >= G) return;
-  float M = -INFINITY;
-#pragma unroll
-  for (int w2 = 0; w2 < kDecodeWaves; ++w2) M = fmaxf(M, sm_m[w2][oc]);
-  float f[kDecodeWaves];
-  float lsum = 0.f;
-#pragma unroll
-  for (int w2 = 0; w2 < kDecodeWaves; ++w2) {
-    const float mw = sm_m[w2][oc];
-    f[w2] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-    lsum += f[w2] * sm_l[w2][oc];
-  }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  constexpr int DPT = D / 16;
-  float acc[DPT];
-#pragma unroll
-  for (int i = 0; i < DPT; ++i) {
-    const int d = dpart * DPT + i;
-    float a = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < kDecodeWaves; ++w2)
-      a += f[w2] * reinterpret_cast<const float*>(smem + w2 * C::WAVE_LDS)[d * 16 + oc];
-    acc[i] = a * inv;
-  }
-  const int hout = kh * G + hg * 16 + oc;
-  if constexpr (SPLIT) {
-    const size_t pi = ((size_t)b * Hq + hout) * Pmax + p;
-    float* op = o_part + pi * D + dpart * DPT;
-#pragma unroll
-    for (int i = 0; i < DPT; i += 4)
-      *reinterpret_cast<f32x4*>(op + i) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
-    if (dpart == 0) {
-      m_part[pi] = M;
-      l_part[pi] = lsum;
+      for (int mt = 0; mt < C::MT; ++mt)
+        *reinterpret_cast<u32x2*>(op + mt * 16) =
+            u32x2{pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv), pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv)};
+      if (lse != nullptr && qg == 0)
+        lse[(size_t)b * Hq + hout] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
     }
+    return;
   } else {
-    uint16_t* op = out + ((size_t)b * Hq + hout) * D + dpart * DPT;
+    __syncthreads();  // every wave is done with its V tile; reuse it for O^T [d][16]
+    float* obuf = reinterpret_cast<float*>(vbuf);
 #pragma unroll
-    for (int i = 0; i < DPT; i += 4)
-      *reinterpret_cast<u32x2*>(op + i) =
-          u32x2{pack_bf16x2(acc[i], acc[i + 1]), pack_bf16x2(acc[i + 2], acc[i + 3])};
-    if (lse != nullptr && dpart == 0)
-      lse[(size_t)b * Hq + hout] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) obuf[(mt * 16 + 4 * qg + r) * 16 + col] = o[mt][r];
+    if (lane < 16) {
+      sm_m[w][lane] = m_run;
+      sm_l[w][lane] = l_run;
+    }
+    __syncthreads();
+
+    constexpr int TPC = NW * kWave / 16;  // threads per head column
+    constexpr int DPT = D / TPC;          // outputs per thread
+    const int t = threadIdx.x;
+    const int oc = t / TPC;
+    const int dpart = t - oc * TPC;
+    if (hg * 16 + oc >= G) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, sm_m[w2][oc]);
+    float f[NW];
+    float lsum = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      const float mw = sm_m[w2][oc];
+      f[w2] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+      lsum += f[w2] * sm_l[w2][oc];
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    float acc[DPT];
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) {
+      const int d = dpart * DPT + i;
+      float a = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2)
+        a += f[w2] * reinterpret_cast<const float*>(smem + w2 * C::WAVE_LDS)[d * 16 + oc];
+      acc[i] = a * inv;
+    }
+    const int hout = kh * G + hg * 16 + oc;
+    if constexpr (SPLIT) {
+      const size_t pi = ((size_t)b * Hq + hout) * Pmax + p;
+      float* op = o_part + pi * D + dpart * DPT;
+#pragma unroll
+      for (int i = 0; i < DPT; i += 4)
+        *reinterpret_cast<f32x4*>(op + i) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
+      if (dpart == 0) {
+        m_part[pi] = M;
+        l_part[pi] = lsum;
+      }
+    } else {
+      uint16_t* op = out + ((size_t)b * Hq + hout) * D + dpart * DPT;
+#pragma unroll
+      for (int i = 0; i < DPT; i += 4)
+        *reinterpret_cast<u32x2*>(op + i) =
+            u32x2{pack_bf16x2(acc[i], acc[i + 1]), pack_bf16x2(acc[i + 2], acc[i + 3])};
+      if (lse != nullptr && dpart == 0)
+        lse[(size_t)b * Hq + hout] = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+    }
   }
 }
 
@@ -342,16 +416,18 @@ template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int n_hg = (G + 15) / 16;
-  const float scale_log2 = a.scale * kLog2e;
-  const dim3 block(kDecodeThreads);
+  float scale_log2 = a.scale * kLog2e;
+  const int negate_q = scale_log2 < 0.f;
+  if (negate_q) scale_log2 = -scale_log2;
+  if (!(scale_log2 >= 1.17549435e-38f)) scale_log2 = 1.17549435e-38f;  // zero (or denormal) scale
   if (a.partition_tokens > 0) {
     const dim3 grid(a.max_partitions, a.num_kv_heads * n_hg, a.batch);
-    hipLaunchKernelGGL((decode_kernel<D, true>), grid, block, 0, stream,
+    hipLaunchKernelGGL((decode_kernel<D, 1, true>), grid, dim3(kWave), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache,
                        a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, a.o_part, a.m_part,
                        a.l_part, a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size,
                        a.num_blocks, a.max_blocks_per_seq, a.partition_tokens, a.max_partitions,
-                       scale_log2);
+                       scale_log2, negate_q, __builtin_ctz((unsigned)a.block_size));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.num_q_heads, a.batch), dim3(256), 0,
@@ -361,11 +437,12 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const dim3 grid(1, a.num_kv_heads * n_hg, a.batch);
-  hipLaunchKernelGGL((decode_kernel<D, false>), grid, block, 0, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache,
-                     a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, nullptr, nullptr,
-                     nullptr, a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size, a.num_blocks,
-                     a.max_blocks_per_seq, 0, 1, scale_log2);
+  hipLaunchKernelGGL((decode_kernel<D, kDirectWaves, false>), grid, dim3(kDirectWaves * kWave), 0,
+                     stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
+                     (const uint16_t*)a.v_cache, a.block_tables, a.seq_lens, (uint16_t*)a.out,
+                     a.lse, nullptr, nullptr, nullptr, a.num_q_heads, a.num_kv_heads, G, n_hg,
+                     a.block_size, a.num_blocks, a.max_blocks_per_seq, 0, 1, scale_log2, negate_q,
+                     __builtin_ctz((unsigned)a.block_size));
   return hipGetLastError();
 }
 

@@ -56,12 +56,15 @@ struct RaggedLoader {
   }
 };
 
+// Rows of one load instruction of a wave never straddle a block (at most 16 aligned rows per
+// instruction, blocks are multiples of 16 rows), so the block id is wave-uniform and comes from
+// the wave's table window.
 struct PagedLoader {
-  const int32_t* trow;  // this request's block-table row
-  int Hkv, kh, D, BS, NB;
-  __device__ __forceinline__ size_t row_offset(int n) const {
-    const int blk = clampi(trow[n / BS], 0, NB - 1);
-    return (((size_t)blk * Hkv + kh) * BS + (n % BS)) * D;
+  int Hkv, kh, D, BS, NB, bs_shift;
+  // row n lies in the same block as the wave-uniform row nb
+  __device__ __forceinline__ size_t row_offset(TableWindow& tw, int nb, int n, int lane) const {
+    const int blk = clampi(tw.get(nb >> bs_shift, lane), 0, NB - 1);
+    return (((size_t)blk * Hkv + kh) * BS + (n & (BS - 1))) * D;
   }
 };
 
@@ -74,7 +77,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
                const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ tables,
                int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
-               int negate_q, int xcd_heads) {
+               int negate_q, int xcd_heads, int bs_shift) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ROWS * C::RSE];
   uint16_t* const k_lds = smem;
@@ -141,7 +144,10 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int lim = causal ? min(row + off, kv - 1) : kv - 1;
 
   const RaggedLoader rl{kv0, Hkv, kh, D};
-  const PagedLoader pl{PAGED ? tables + (size_t)b * max_blocks : nullptr, Hkv, kh, D, BS, NB};
+  const PagedLoader pl{Hkv, kh, D, BS, NB, bs_shift};
+  TableWindow tw;
+  if constexpr (PAGED) tw.init(tables + (size_t)b * max_blocks, max_blocks, 0, lane);
+  static_assert(kWave * 16 / (2 * D) <= 16, "a wave's load rows must stay inside one block");
 
   u32x4 kpre[C::UPT], vpre[C::UPT];
   auto fetch = [&](int n0) {
@@ -150,9 +156,15 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const int u = i * kPrefillThreads + tid;
       const int rr = u / C::UPR;
       const int cu = u - rr * C::UPR;
-      const int n = min(n0 + rr, kv - 1);
       size_t ro;
-      if constexpr (PAGED) ro = pl.row_offset(n); else ro = rl.row_offset(n);
+      if constexpr (PAGED) {
+        // clamp whole instructions (not single rows) so the block index stays wave-uniform
+        const int nb = min(n0 + (i * kPrefillThreads + (tid & ~63)) / C::UPR, kv - 1);
+        const int n = min(n0 + rr, kv - 1);
+        ro = pl.row_offset(tw, nb, n, lane);
+      } else {
+        ro = rl.row_offset(min(n0 + rr, kv - 1));
+      }
       kpre[i] = load16(k + ro + cu * 8);
       vpre[i] = load16(v + ro + cu * 8);
     }
@@ -293,7 +305,8 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
                      a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
-                     a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads);
+                     a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads,
+                     a.block_size > 0 ? __builtin_ctz((unsigned)a.block_size) : 0);
   return hipGetLastError();
 }
 
