@@ -6,17 +6,22 @@
 // path) 512-token partitions whose statistics a second kernel merges by log-sum-exp.
 //
 // MI355X design. Decode moves every K/V byte exactly once, so the kernel is an HBM stream:
-//   * work-group = 4 waves on one (sequence, kv head, q-head group of <= 16, partition);
-//     each wave walks 32-token chunks (two 16-token half pages) round robin and keeps its own
-//     running (m, l, O); the four are combined through LDS at the end;
+//   * a wave streams 32-token chunks (two 16-token half pages) of one (sequence, kv head, group
+//     of <= 16 q heads) with the next chunk's loads already in flight while one is processed;
+//     split-KV: one single-wave work-group per partition; direct: 4 waves per sequence take
+//     chunks round robin and are combined through LDS at the end;
 //   * QK^T on a 16x16x32 bf16 MFMA with the K half page as the A operand (rows = 16 tokens, loaded
 //     straight from HBM in 16-byte pieces) and the GQA group's q rows as B (16 columns);
 //   * the score tile lands in the layout the PV MFMA needs for its B operand: each lane already
 //     holds 8 probabilities of one head, so P never moves between lanes;
-//   * V is read from HBM in fully contiguous 1 KiB wave loads, staged row-major in a per-wave
-//     LDS tile with an 8-byte row pad, and read back column-wise as the PV MFMA's A operand (V^T);
-//   * softmax runs in the log2 domain (scale * log2 e folded into one multiply, v_exp_f32);
-//     slots past the sequence length are masked by selection (their bits may be NaN).
+//   * V is read from HBM in contiguous 1 KiB wave loads, staged row-major in a per-wave LDS tile
+//     (row pad chosen so transpose reads hit distinct banks) and read back with the gfx950
+//     transpose read (ds_read_b64_tr_b16) as V^T, the PV MFMA's A operand;
+//   * softmax runs in the log2 domain with the scale folded into one FMA before v_exp_f32; the
+//     running max is raised only when it grows by more than 2^8 (a wave-uniform branch);
+//   * block ids come from a per-wave table window read with v_readlane, so forming an address
+//     never waits on a table load queued behind in-flight data;
+//   * slots past the sequence length are masked by selection (their bits may be NaN).
 #include <math.h>
 
 #include "common.h"
@@ -24,7 +29,7 @@
 
 namespace pkv {
 
-constexpr int kDirectWaves = 4;  // waves per work-group on the direct path (one per split partition)
+constexpr int kDirectWaves = 4;  // waves per work-group on the direct path (split: one wave)
 constexpr float kRescaleLog2 = 8.0f;  // raise a running max only when exceeded by more than this
 constexpr int kPrefetch = 2;          // 32-token chunks per wave in flight (loads issued ahead)
 
