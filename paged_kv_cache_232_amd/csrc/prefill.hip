@@ -71,7 +71,7 @@ struct PagedLoader {
 // scale_log2 > 0 always: the host folds a negative scale into negate_q (an exact sign flip of q)
 // and replaces a zero scale by the smallest normal float (every score then rounds to 2^0 = 1).
 template <int D, bool PAGED>
-__global__ void __launch_bounds__(kPrefillThreads)
+__global__ void __launch_bounds__(kPrefillThreads, D <= 128 ? 2 : 1)
 prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
                const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
