@@ -44,7 +44,8 @@ struct PrefillCfg {
   static constexpr int UPR = D / 8;                 // 16-byte units per row
   static constexpr int UNITS = BN * UPR;            // units per tile (K or V)
   static constexpr int UPT = UNITS / kPrefillThreads;  // units per thread
-  static constexpr int LDS_ROWS = (2 * BN > kBM) ? 2 * BN : kBM;  // K+V tiles, or the output tile
+  // two K+V tile buffers (double buffering), later reused for the output tile
+  static constexpr int LDS_ROWS = (4 * BN > kBM) ? 4 * BN : kBM;
   static_assert(UNITS % kPrefillThreads == 0, "tile units must divide evenly");
 };
 
@@ -80,8 +81,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                int negate_q, int xcd_heads, int bs_shift) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ROWS * C::RSE];
-  uint16_t* const k_lds = smem;
-  uint16_t* const v_lds = smem + C::BN * C::RSE;
+  // buffer j (0/1): K rows at smem + 2*j*BN*RSE, V rows BN*RSE further
 
   // block x -> q head: heads sharing a kv head go to the same XCD (round-robin x % 8)
   int h = blockIdx.x;
@@ -150,7 +150,45 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   static_assert(kWave * 16 / (2 * D) <= 16, "a wave's load rows must stay inside one block");
 
   u32x4 kpre[C::UPT], vpre[C::UPT];
+  // Tile-invariant parts of this thread's load and stage addresses. Load i of a wave covers
+  // consecutive rows starting at row wrow(i) of the tile (at most 16, inside one block).
+  const int w_u0 = __builtin_amdgcn_readfirstlane(tid & ~63);  // first unit of this wave
+  int loff[C::UPT];  // element offset of this thread's 16-byte unit from its instruction's base
+#pragma unroll
+  for (int i = 0; i < C::UPT; ++i) {
+    const int u = i * kPrefillThreads + tid;
+    const int rr = u / C::UPR;
+    const int cu = u - rr * C::UPR;
+    if constexpr (PAGED) {
+      loff[i] = (rr - (i * kPrefillThreads + w_u0) / C::UPR) * D + cu * 8;
+    } else {
+      loff[i] = rr * (Hkv * D) + cu * 8;
+    }
+  }
   auto fetch = [&](int n0) {
+    if (n0 + C::BN <= kv) {
+      // whole tile inside the request: one scalar base per instruction (paged) or per tile
+      if constexpr (PAGED) {
+#pragma unroll
+        for (int i = 0; i < C::UPT; ++i) {
+          const int nw = n0 + (i * kPrefillThreads + w_u0) / C::UPR;
+          const int blk = clampi(tw.get(nw >> bs_shift, lane), 0, NB - 1);
+          const uint16_t* kb = k + (((size_t)blk * Hkv + kh) * BS + (nw & (BS - 1))) * D;
+          const uint16_t* vb = v + (((size_t)blk * Hkv + kh) * BS + (nw & (BS - 1))) * D;
+          kpre[i] = load16(kb + loff[i]);
+          vpre[i] = load16(vb + loff[i]);
+        }
+      } else {
+        const size_t tb = ((size_t)(kv0 + n0) * Hkv + kh) * D;
+#pragma unroll
+        for (int i = 0; i < C::UPT; ++i) {
+          kpre[i] = load16(k + tb + loff[i]);
+          vpre[i] = load16(v + tb + loff[i]);
+        }
+      }
+      return;
+    }
+    // the request's last tile: rows past the end re-read the last row
 #pragma unroll
     for (int i = 0; i < C::UPT; ++i) {
       const int u = i * kPrefillThreads + tid;
@@ -159,7 +197,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       size_t ro;
       if constexpr (PAGED) {
         // clamp whole instructions (not single rows) so the block index stays wave-uniform
-        const int nb = min(n0 + (i * kPrefillThreads + (tid & ~63)) / C::UPR, kv - 1);
+        const int nb = min(n0 + (i * kPrefillThreads + w_u0) / C::UPR, kv - 1);
         const int n = min(n0 + rr, kv - 1);
         ro = pl.row_offset(tw, nb, n, lane);
       } else {
@@ -169,16 +207,29 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       vpre[i] = load16(v + ro + cu * 8);
     }
   };
-  auto stash = [&](int n0) {
+  auto stash = [&](int n0, int buf) {
+    uint16_t* const k_lds = smem + 2 * buf * C::BN * C::RSE;
+    uint16_t* const v_lds = k_lds + C::BN * C::RSE;
+    if (n0 + C::BN <= kv) {
 #pragma unroll
-    for (int i = 0; i < C::UPT; ++i) {
-      const int u = i * kPrefillThreads + tid;
-      const int rr = u / C::UPR;
-      const int cu = u - rr * C::UPR;
-      u32x4 vv = vpre[i];
-      if (n0 + rr >= kv) vv = u32x4{0, 0, 0, 0};  // rows past the end never carry NaN into PV
-      *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[i];
-      *reinterpret_cast<u32x4*>(v_lds + rr * C::RSE + cu * 8) = vv;
+      for (int i = 0; i < C::UPT; ++i) {
+        const int u = i * kPrefillThreads + tid;
+        const int rr = u / C::UPR;
+        const int cu = u - rr * C::UPR;
+        *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[i];
+        *reinterpret_cast<u32x4*>(v_lds + rr * C::RSE + cu * 8) = vpre[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::UPT; ++i) {
+        const int u = i * kPrefillThreads + tid;
+        const int rr = u / C::UPR;
+        const int cu = u - rr * C::UPR;
+        u32x4 vv = vpre[i];
+        if (n0 + rr >= kv) vv = u32x4{0, 0, 0, 0};  // rows past the end never carry NaN into PV
+        *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[i];
+        *reinterpret_cast<u32x4*>(v_lds + rr * C::RSE + cu * 8) = vv;
+      }
     }
   };
 
@@ -188,14 +239,21 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int tr_row = 4 * (grp >> 1) + ((lane & 15) >> 2);
   const int tr_col = 16 * (grp & 1) + 4 * (lane & 3);
 
-  if (n_kt > 0) fetch(0);
+  // Double-buffered tiles: tile t+1 is staged into the other buffer while tile t is consumed and
+  // tile t+2's loads are already in flight; one barrier per tile.
+  if (n_kt > 0) {
+    fetch(0);
+    stash(0, 0);
+    if (n_kt > 1) fetch(C::BN);
+  }
+  // last key any row of this wave can see (causal): tiles past it are skipped by the wave
+  const int wave_last_key = causal ? m0 + w * 32 + 31 + off : 0x7fffffff;
   for (int t = 0; t < n_kt; ++t) {
     const int n0 = t * C::BN;
-    __syncthreads();  // previous tile fully consumed
-    stash(n0);
-    __syncthreads();
-    if (t + 1 < n_kt) fetch(n0 + C::BN);
-
+    __syncthreads();  // tile t staged by every wave; tile t-1's buffer no longer read
+    const uint16_t* const k_lds = smem + 2 * (t & 1) * C::BN * C::RSE;
+    const uint16_t* const v_lds = k_lds + C::BN * C::RSE;
+    if (n0 <= wave_last_key) {
     // S^T tile: lane holds keys n0 + mt*32 + 8*(r/4) + 4*half + r%4 of query qcol (raw scores)
     f32x16 s[C::MT];
 #pragma unroll
@@ -214,20 +272,20 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // mask only tiles crossing the ragged end or this wave's causal diagonal
     const bool need_mask = (n0 + C::BN > kv) || (causal && n0 + C::BN - 1 > m0 + w * 32 + off);
     if (need_mask) {
+      // key n0 + mt*32 + 8*(r/4) + 4*half + r%4 is visible iff mt*32 + 8*(r/4) + r%4 <= thr
+      const int thr = lim - n0 - 4 * half;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = n0 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > lim) s[mt][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (mt * 32 + 8 * (r >> 2) + (r & 3) > thr) s[mt][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(mx);
     const float tmax = mx * scale_log2;
     if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleLog2) != 0) {
       const float m_new = fmaxf(m_run, tmax);
@@ -263,10 +321,15 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const u32x2 hi = lds_read_tr16(vp + 8 * C::RSE);
         o[dt] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[st], o[dt]);
       }
+    }
+    if (t + 1 < n_kt) {
+      stash(n0 + C::BN, (t + 1) & 1);
+      if (t + 2 < n_kt) fetch(n0 + 2 * C::BN);
+    }
   }
 
   // normalise, stage the wave's 32 rows in LDS, then write whole rows with 16-byte stores
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_xor32(l_run);
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   __syncthreads();
   uint16_t* const ost = smem + w * 32 * C::RSE;
