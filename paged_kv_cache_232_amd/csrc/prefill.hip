@@ -40,12 +40,17 @@ struct PrefillCfg {
   static constexpr int MT = BN / 32;                // 32-key tiles of S^T
   static constexpr int PS = BN / 16;                // 16-key steps of PV
   static constexpr int DT = D / 32;                 // 32-wide d tiles of O^T
-  static constexpr int RSE = D + 8;                 // LDS row stride in elements (16-byte pad)
+  // LDS row strides in elements. K rows (read 16 bytes per lane, 8 rows per LDS cycle) take a
+  // 16-byte pad; V rows (transpose-read 8 bytes per lane, 4 rows x 64 bytes per 32 lanes) take a
+  // 64-byte pad, which spreads those rows over all 64 banks. Both measured conflict-free.
+  static constexpr int RSE = D + 8;                 // K rows and the output tile
+  static constexpr int RSV = D + 32;                // V rows
+  static constexpr int BUF = BN * (RSE + RSV);      // one K+V tile buffer
   static constexpr int UPR = D / 8;                 // 16-byte units per row
   static constexpr int UNITS = BN * UPR;            // units per tile (K or V)
   static constexpr int UPT = UNITS / kPrefillThreads;  // units per thread
   // two K+V tile buffers (double buffering), later reused for the output tile
-  static constexpr int LDS_ROWS = (4 * BN > kBM) ? 4 * BN : kBM;
+  static constexpr int LDS_ELEMS = (2 * BUF > kBM * RSE) ? 2 * BUF : kBM * RSE;
   static_assert(UNITS % kPrefillThreads == 0, "tile units must divide evenly");
 };
 
@@ -80,8 +85,8 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
                int negate_q, int xcd_heads, int bs_shift) {
   using C = PrefillCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ROWS * C::RSE];
-  // buffer j (0/1): K rows at smem + 2*j*BN*RSE, V rows BN*RSE further
+  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+  // buffer j (0/1): K rows at smem + j*BUF, V rows BN*RSE further
 
   // block x -> q head: heads sharing a kv head go to the same XCD (round-robin x % 8)
   int h = blockIdx.x;
@@ -208,7 +213,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   };
   auto stash = [&](int n0, int buf) {
-    uint16_t* const k_lds = smem + 2 * buf * C::BN * C::RSE;
+    uint16_t* const k_lds = smem + buf * C::BUF;
     uint16_t* const v_lds = k_lds + C::BN * C::RSE;
     if (n0 + C::BN <= kv) {
 #pragma unroll
@@ -217,7 +222,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int rr = u / C::UPR;
         const int cu = u - rr * C::UPR;
         *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[i];
-        *reinterpret_cast<u32x4*>(v_lds + rr * C::RSE + cu * 8) = vpre[i];
+        *reinterpret_cast<u32x4*>(v_lds + rr * C::RSV + cu * 8) = vpre[i];
       }
     } else {
 #pragma unroll
@@ -228,7 +233,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         u32x4 vv = vpre[i];
         if (n0 + rr >= kv) vv = u32x4{0, 0, 0, 0};  // rows past the end never carry NaN into PV
         *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[i];
-        *reinterpret_cast<u32x4*>(v_lds + rr * C::RSE + cu * 8) = vv;
+        *reinterpret_cast<u32x4*>(v_lds + rr * C::RSV + cu * 8) = vv;
       }
     }
   };
@@ -251,7 +256,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int t = 0; t < n_kt; ++t) {
     const int n0 = t * C::BN;
     __syncthreads();  // tile t staged by every wave; tile t-1's buffer no longer read
-    const uint16_t* const k_lds = smem + 2 * (t & 1) * C::BN * C::RSE;
+    const uint16_t* const k_lds = smem + (t & 1) * C::BUF;
     const uint16_t* const v_lds = k_lds + C::BN * C::RSE;
     if (n0 <= wave_last_key) {
     // S^T tile: lane holds keys n0 + mt*32 + 8*(r/4) + 4*half + r%4 of query qcol (raw scores)
@@ -316,9 +321,9 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int st = 0; st < C::PS; ++st)
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const uint16_t* vp = v_lds + (16 * st + tr_row) * C::RSE + dt * 32 + tr_col;
+        const uint16_t* vp = v_lds + (16 * st + tr_row) * C::RSV + dt * 32 + tr_col;
         const u32x2 lo = lds_read_tr16(vp);
-        const u32x2 hi = lds_read_tr16(vp + 8 * C::RSE);
+        const u32x2 hi = lds_read_tr16(vp + 8 * C::RSV);
         o[dt] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[st], o[dt]);
       }
     }
