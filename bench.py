@@ -17,6 +17,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -37,6 +38,37 @@ from workloads import CONFIGS, make_config  # noqa: E402
 HBM_PEAK_GBS = 8000.0                          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # dense bf16 MFMA, 2516.6 TFLOP/s
 METRIC = "decode KV GB/s (% HBM peak); ragged-prefill bf16 TFLOP/s (% MFMA peak)"
+
+
+# ----------------------------------------------------------------------------------------------
+# Measured HBM traffic per call (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, the factors a plain 1 GiB
+# copy gives; profiles/hot_path_step_hbm_traffic.md). Each figure holds only while the kernel sources
+# it was taken from are unchanged: the sha256 over those files is checked at run time, and a
+# mismatch reports traffic as null.
+CSRC = os.path.join(ROOT, "paged_kv_cache_232_amd", "csrc")
+TRAFFIC = {
+    "scatter5": (("cache.hip",), "805e9b81e70263d7", 71277094),
+    "paged5": (("prefill.hip", "common.h"), "663b4e8683b222be", 1603863987),
+    "ragged2": (("prefill.hip", "common.h"), "663b4e8683b222be", 236893215),
+    "decode3": (("decode.hip", "common.h"), "11576333e723b3f5", 1039576786),
+    "decode4": (("decode.hip", "common.h"), "11576333e723b3f5", 2222327894),
+    "decode3_direct": (("decode.hip", "common.h"), "11576333e723b3f5", 1019433720),
+}
+
+
+def sources_sha(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(call):
+    if call not in TRAFFIC:
+        return None
+    files, sha, nbytes = TRAFFIC[call]
+    return nbytes if sources_sha(files) == sha else None
 
 
 # ----------------------------------------------------------------------------------------------
@@ -258,6 +290,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library's hot path runs on a single MI355X and no "
@@ -286,7 +320,8 @@ def main():
         peak = HBM_PEAK_GBS if c.kind == "hbm" else MFMA_BF16_PEAK_TFLOPS
         r = c.rate(avg)
         return {"call": c.name, "avg_ms": round(avg, 5), "median_ms": round(med, 5), "work": c.work,
-                "rate": round(r, 2), "unit": c.unit, "frac_of_peak": round(r / peak, 4)}
+                "rate": round(r, 2), "unit": c.unit, "frac_of_peak": round(r / peak, 4),
+                "hbm_traffic_bytes": measured_traffic(k)}
 
     per = {k: summary(k) for k in STEP + ["decode3_direct", "decode3_split"]}
     dec_ms = sum(statistics.fmean(cases[k].ms) for k in ("decode3", "decode4"))
@@ -327,11 +362,11 @@ def main():
         "roofline": {"bound": "hbm" if dc.kind == "hbm" else "mfma", "kernel": dc.name,
                      "achieved": round(dach, 2), "peak": dpeak,
                      "unit": "GB/s" if dc.kind == "hbm" else "TFLOP/s", "frac": round(dach / dpeak, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(dom)},
         "per_call": per,
         "wall_s_timed": round(wall, 4),
     }
-    line["cpu_baseline"] = cpu_baseline(meta)
+    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(meta)
     print(json.dumps(line), flush=True)
 
 
