@@ -18,10 +18,13 @@ SOURCES = ["api.cpp", "cache.hip", "decode.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled for all device code (hipcc -O3 would otherwise form them
-# from plain float code).
+# from plain float code). MFMA results are kept in VGPR form: with the accumulator-register form
+# the allocator copied the whole output accumulator between AGPRs and VGPRs on every loop
+# iteration of the head_dim-256 kernels.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -111,6 +111,11 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Keeps the compiler from moving memory operations across this point. Loads that a loop keeps in
+// flight across iterations must be issued in the same order before the loop as inside it, or the
+// wait-count pass cannot tell their order at the loop head and waits for all of them.
+__device__ __forceinline__ void memory_order_point() { asm volatile("" ::: "memory"); }
+
 template <typename T>
 __device__ __forceinline__ T clampi(T x, T lo, T hi) {
   return x < lo ? lo : (x > hi ? hi : x);

@@ -21,6 +21,8 @@
 //   * q tiles are issued last-first (the longest causal rows start first).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -49,6 +51,10 @@ struct PrefillCfg {
   static constexpr int UPR = D / 8;                 // 16-byte units per row
   static constexpr int UNITS = BN * UPR;            // units per tile (K or V)
   static constexpr int UPT = UNITS / kPrefillThreads;  // units per thread
+  // kv tiles held in registers between their loads and their LDS stage: the loads of tile t+PF+1
+  // are issued while tile t is consumed. head_dim 256 runs one wave per SIMD, so nothing else
+  // hides its load latency: it keeps two tiles in flight.
+  static constexpr int PF = (D >= 256) ? 2 : 1;
   // two K+V tile buffers (double buffering), later reused for the output tile
   static constexpr int LDS_ELEMS = (2 * BUF > kBM * RSE) ? 2 * BUF : kBM * RSE;
   static_assert(UNITS % kPrefillThreads == 0, "tile units must divide evenly");
@@ -63,14 +69,19 @@ struct RaggedLoader {
 };
 
 // Rows of one load instruction of a wave never straddle a block (at most 16 aligned rows per
-// instruction, blocks are multiples of 16 rows), so the block id is wave-uniform and comes from
-// the wave's table window.
+// instruction, blocks are multiples of 16 rows), so the block id is wave-uniform: it is read with a
+// scalar load from the request's table row. (A vector table load between the tile loads would make
+// the compiler wait for every tile load in flight before forming the next address.)
 struct PagedLoader {
+  const int32_t* row;  // the request's block-table row (uniform)
   int Hkv, kh, D, BS, NB, bs_shift;
+  // physical block of the wave-uniform key nb
+  __device__ __forceinline__ int block_of(int nb) const {
+    return clampi(row[__builtin_amdgcn_readfirstlane(nb) >> bs_shift], 0, NB - 1);
+  }
   // row n lies in the same block as the wave-uniform row nb
-  __device__ __forceinline__ size_t row_offset(TableWindow& tw, int nb, int n, int lane) const {
-    const int blk = clampi(tw.get(nb >> bs_shift, lane), 0, NB - 1);
-    return (((size_t)blk * Hkv + kh) * BS + (n & (BS - 1))) * D;
+  __device__ __forceinline__ size_t row_offset(int nb, int n) const {
+    return (((size_t)block_of(nb) * Hkv + kh) * BS + (n & (BS - 1))) * D;
   }
 };
 
@@ -149,92 +160,46 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int lim = causal ? min(row + off, kv - 1) : kv - 1;
 
   const RaggedLoader rl{kv0, Hkv, kh, D};
-  const PagedLoader pl{Hkv, kh, D, BS, NB, bs_shift};
-  TableWindow tw;
-  if constexpr (PAGED) tw.init(tables + (size_t)b * max_blocks, max_blocks, 0, lane);
+  const PagedLoader pl{tables + (size_t)b * max_blocks, Hkv, kh, D, BS, NB, bs_shift};
   static_assert(kWave * 16 / (2 * D) <= 16, "a wave's load rows must stay inside one block");
 
-  u32x4 kpre[C::UPT], vpre[C::UPT];
-  // Tile-invariant parts of this thread's load and stage addresses. Load i of a wave covers
-  // consecutive rows starting at row wrow(i) of the tile (at most 16, inside one block).
+  u32x4 kpre[C::PF][C::UPT], vpre[C::PF][C::UPT];
   const int w_u0 = __builtin_amdgcn_readfirstlane(tid & ~63);  // first unit of this wave
-  int loff[C::UPT];  // element offset of this thread's 16-byte unit from its instruction's base
-#pragma unroll
-  for (int i = 0; i < C::UPT; ++i) {
-    const int u = i * kPrefillThreads + tid;
-    const int rr = u / C::UPR;
-    const int cu = u - rr * C::UPR;
-    if constexpr (PAGED) {
-      loff[i] = (rr - (i * kPrefillThreads + w_u0) / C::UPR) * D + cu * 8;
-    } else {
-      loff[i] = rr * (Hkv * D) + cu * 8;
-    }
-  }
-  auto fetch = [&](int n0) {
-    if (n0 + C::BN <= kv) {
-      // whole tile inside the request: one scalar base per instruction (paged) or per tile
-      if constexpr (PAGED) {
-#pragma unroll
-        for (int i = 0; i < C::UPT; ++i) {
-          const int nw = n0 + (i * kPrefillThreads + w_u0) / C::UPR;
-          const int blk = clampi(tw.get(nw >> bs_shift, lane), 0, NB - 1);
-          const uint16_t* kb = k + (((size_t)blk * Hkv + kh) * BS + (nw & (BS - 1))) * D;
-          const uint16_t* vb = v + (((size_t)blk * Hkv + kh) * BS + (nw & (BS - 1))) * D;
-          kpre[i] = load16(kb + loff[i]);
-          vpre[i] = load16(vb + loff[i]);
-        }
-      } else {
-        const size_t tb = ((size_t)(kv0 + n0) * Hkv + kh) * D;
-#pragma unroll
-        for (int i = 0; i < C::UPT; ++i) {
-          kpre[i] = load16(k + tb + loff[i]);
-          vpre[i] = load16(v + tb + loff[i]);
-        }
-      }
-      return;
-    }
-    // the request's last tile: rows past the end re-read the last row
+  // Loads of tile rows n0 .. n0+BN-1; rows past the request's end re-read its last row (their
+  // probabilities are exactly 0). Every call issues the same loads in the same order, whatever
+  // n0 is, so the wait before each stage counts exactly the loads still needed.
+  auto fetch = [&](int n0, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
     for (int i = 0; i < C::UPT; ++i) {
       const int u = i * kPrefillThreads + tid;
       const int rr = u / C::UPR;
       const int cu = u - rr * C::UPR;
+      const int n = min(n0 + rr, kv - 1);
       size_t ro;
       if constexpr (PAGED) {
-        // clamp whole instructions (not single rows) so the block index stays wave-uniform
+        // the instruction's first row: wave-uniform, in the same block as every row it loads
         const int nb = min(n0 + (i * kPrefillThreads + w_u0) / C::UPR, kv - 1);
-        const int n = min(n0 + rr, kv - 1);
-        ro = pl.row_offset(tw, nb, n, lane);
+        ro = pl.row_offset(nb, n);
       } else {
-        ro = rl.row_offset(min(n0 + rr, kv - 1));
+        ro = rl.row_offset(n);
       }
-      kpre[i] = load16(k + ro + cu * 8);
-      vpre[i] = load16(v + ro + cu * 8);
+      kpre[sl][i] = load16(k + ro + cu * 8);
+      vpre[sl][i] = load16(v + ro + cu * 8);
+      memory_order_point();
     }
   };
-  auto stash = [&](int n0, int buf) {
+  auto stash = [&](int buf, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
     uint16_t* const k_lds = smem + buf * C::BUF;
     uint16_t* const v_lds = k_lds + C::BN * C::RSE;
-    if (n0 + C::BN <= kv) {
 #pragma unroll
-      for (int i = 0; i < C::UPT; ++i) {
-        const int u = i * kPrefillThreads + tid;
-        const int rr = u / C::UPR;
-        const int cu = u - rr * C::UPR;
-        *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[i];
-        *reinterpret_cast<u32x4*>(v_lds + rr * C::RSV + cu * 8) = vpre[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::UPT; ++i) {
-        const int u = i * kPrefillThreads + tid;
-        const int rr = u / C::UPR;
-        const int cu = u - rr * C::UPR;
-        u32x4 vv = vpre[i];
-        if (n0 + rr >= kv) vv = u32x4{0, 0, 0, 0};  // rows past the end never carry NaN into PV
-        *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[i];
-        *reinterpret_cast<u32x4*>(v_lds + rr * C::RSV + cu * 8) = vv;
-      }
+    for (int i = 0; i < C::UPT; ++i) {
+      const int u = i * kPrefillThreads + tid;
+      const int rr = u / C::UPR;
+      const int cu = u - rr * C::UPR;
+      *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[sl][i];
+      *reinterpret_cast<u32x4*>(v_lds + rr * C::RSV + cu * 8) = vpre[sl][i];
     }
   };
 
@@ -244,16 +209,21 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int tr_row = 4 * (grp >> 1) + ((lane & 15) >> 2);
   const int tr_col = 16 * (grp & 1) + 4 * (lane & 3);
 
-  // Double-buffered tiles: tile t+1 is staged into the other buffer while tile t is consumed and
-  // tile t+2's loads are already in flight; one barrier per tile.
+  // Double-buffered LDS tiles: tile t+1 is staged into the other buffer while tile t is consumed,
+  // with the loads of tiles t+2 .. t+PF+1 already in flight; one barrier per tile. Register slot
+  // (tile % PF) holds a tile from its loads to its stage.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, (C::PF > 1) ? 1 : 0>;
   if (n_kt > 0) {
-    fetch(0);
-    stash(0, 0);
-    if (n_kt > 1) fetch(C::BN);
+    fetch(0, S0{});
+    stash(0, S0{});
+    fetch(C::BN, S1{});
+    if constexpr (C::PF > 1) fetch(2 * C::BN, S0{});
   }
   // last key any row of this wave can see (causal): tiles past it are skipped by the wave
   const int wave_last_key = causal ? m0 + w * 32 + 31 + off : 0x7fffffff;
-  for (int t = 0; t < n_kt; ++t) {
+  // one kv tile; slot_c is the register slot of tile t+1
+  auto step = [&](int t, auto slot_c) {
     const int n0 = t * C::BN;
     __syncthreads();  // tile t staged by every wave; tile t-1's buffer no longer read
     const uint16_t* const k_lds = smem + (t & 1) * C::BUF;
@@ -327,9 +297,24 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         o[dt] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[st], o[dt]);
       }
     }
-    if (t + 1 < n_kt) {
-      stash(n0 + C::BN, (t + 1) & 1);
-      if (t + 2 < n_kt) fetch(n0 + 2 * C::BN);
+    // Unconditional, also after the last tile (a stage nobody reads, loads of clamped rows), so
+    // every path into the next step has issued the same loads.
+    stash((t + 1) & 1, slot_c);
+    fetch(n0 + (1 + C::PF) * C::BN, slot_c);
+  };
+  if (n_kt > 0) {
+    if constexpr (C::PF == 1) {
+      int t = 0;
+      do {
+        step(t, S0{});
+      } while (++t < n_kt);
+    } else {
+      for (int t = 0;; t += 2) {
+        step(t, S1{});
+        if (t + 1 >= n_kt) break;
+        step(t + 1, S0{});
+        if (t + 2 >= n_kt) break;
+      }
     }
   }
 
@@ -359,6 +344,291 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Variant with 16 query rows per wave on v_mfma_f32_16x16x32_bf16: 8 waves x 16 rows = the same
+// 128-row q tile, but each wave holds half the output accumulator and half the q rows, so two
+// waves fit on a SIMD at head_dim 256 (one wave's LDS and load latency is hidden by the other's
+// MFMA work). Each wave still reads the whole K / V tile from LDS, so LDS traffic per FLOP is
+// twice the 32-row form's.
+//   S^T = K Q^T per 16-key tile: A = 16 K rows x 32 d (LDS), B = the wave's Q rows (registers);
+//     lane l holds keys 16*kt + 4*(l/16) + r of query l%16.
+//   O^T += V^T P^T per 32-key step: the lane's 8 probabilities (keys 4*(l/16) + j and
+//     16 + 4*(l/16) + j of the step) are its B operand as they stand; the A operand takes V^T
+//     with the same key order from two LDS transpose reads.
+constexpr int kP16Waves = 8;
+constexpr int kP16Threads = kP16Waves * kWave;
+constexpr int kP16BM = 16 * kP16Waves;  // query rows per work-group
+static_assert(kP16BM == kBM, "both prefill forms use the same q tile");
+
+template <int D>
+struct P16Cfg {
+  static constexpr int BN = (D >= 256) ? 32 : 64;  // keys per kv tile
+  static constexpr int KT = BN / 16;               // 16-key tiles of S^T
+  static constexpr int KS = D / 32;                // 32-wide d steps of QK^T
+  static constexpr int PS = BN / 32;               // 32-key steps of PV
+  static constexpr int DT = D / 16;                // 16-wide d tiles of O^T
+  // LDS row strides in elements. K rows are read 16 bytes per lane, 16 rows per LDS cycle: a
+  // 16-byte pad. V rows are transpose-read 32 bytes per row, 8 rows per LDS cycle: a 32-byte pad.
+  static constexpr int RSE = D + 8;                // K rows and the output tile
+  static constexpr int RSV = D + 16;               // V rows
+  static constexpr int BUF = BN * (RSE + RSV);     // one K+V tile buffer
+  static constexpr int UPR = D / 8;                // 16-byte units per row
+  static constexpr int UNITS = BN * UPR;           // units per tile (K or V)
+  static constexpr int UPT = UNITS / kP16Threads;  // units per thread
+  static constexpr int PF = (D >= 256) ? 2 : 1;    // kv tiles in flight in registers
+  static constexpr int LDS_ELEMS = (2 * BUF > kP16BM * RSE) ? 2 * BUF : kP16BM * RSE;
+  static_assert(UNITS % kP16Threads == 0, "tile units must divide evenly");
+  static_assert(kWave / UPR <= 16, "a wave's load rows must stay inside one block");
+};
+
+template <int D, bool PAGED>
+__global__ void __launch_bounds__(kP16Threads, 2)
+prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                 const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
+                 const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
+                 const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ tables,
+                 int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
+                 int negate_q, int xcd_heads, int bs_shift) {
+  using C = P16Cfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+  // buffer j (0/1): K rows at smem + j*BUF, V rows BN*RSE further; the output tile reuses it
+
+  int h = blockIdx.x;
+  if (xcd_heads > 0) h = (blockIdx.x & 7) * xcd_heads + (blockIdx.x >> 3);
+  const int b = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int kh = h / G;
+
+  const int q0 = qo_indptr[b];
+  const int qo = qo_indptr[b + 1] - q0;
+  int kv;
+  int64_t kv0 = 0;
+  if constexpr (PAGED) {
+    kv = clampi(kv_lens[b], 0, max_blocks * BS);
+  } else {
+    kv0 = kv_indptr[b];
+    kv = kv_indptr[b + 1] - (int)kv0;
+  }
+  const int n_qt = (qo + kP16BM - 1) / kP16BM;
+  const int qt = n_qt - 1 - (int)blockIdx.z;  // last tile first
+  if (qt < 0) return;
+  const int m0 = qt * kP16BM;
+  const int off = kv - qo;  // row i sits at key position i + off
+
+  int kv_end = kv;
+  if (causal) kv_end = min(kv, m0 + kP16BM + off);
+  const int n_kt = kv_end > 0 ? (kv_end + C::BN - 1) / C::BN : 0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int qcol = lane & 15;  // query of this lane within the wave
+  const int grp = lane >> 4;   // 0..3
+  const int row = m0 + w * 16 + qcol;
+  const bool row_ok = row < qo;
+
+  // Q^T operand: lane holds Q[row][32*ks + 8*grp .. +8]
+  bf16x8 qreg[C::KS];
+  {
+    const int r = row_ok ? row : (qo - 1);
+    const uint16_t* qp = q + ((size_t)(q0 + r) * Hq + h) * D + 8 * grp;
+    const uint32_t flip = negate_q ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 x = load16(qp + ks * 32);
+      x ^= u32x4{flip, flip, flip, flip};
+      qreg[ks] = as_bf16x8(x);
+    }
+  }
+
+  f32x4 o[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // log2 units
+  float l_run = 0.f;
+  const int lim = causal ? min(row + off, kv - 1) : kv - 1;
+
+  const RaggedLoader rl{kv0, Hkv, kh, D};
+  const PagedLoader pl{tables + (size_t)b * max_blocks, Hkv, kh, D, BS, NB, bs_shift};
+
+  u32x4 kpre[C::PF][C::UPT], vpre[C::PF][C::UPT];
+  const int w_u0 = __builtin_amdgcn_readfirstlane(tid & ~63);  // first unit of this wave
+  // Loads of tile rows n0 .. n0+BN-1; rows past the request's end re-read its last row (their
+  // probabilities are exactly 0). Every call issues the same loads in the same order, whatever
+  // n0 is, so the wait before each stage counts exactly the loads still needed.
+  auto fetch = [&](int n0, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
+#pragma unroll
+    for (int i = 0; i < C::UPT; ++i) {
+      const int u = i * kP16Threads + tid;
+      const int rr = u / C::UPR;
+      const int cu = u - rr * C::UPR;
+      const int n = min(n0 + rr, kv - 1);
+      size_t ro;
+      if constexpr (PAGED) {
+        // the instruction's first row: wave-uniform, in the same block as every row it loads
+        const int nb = min(n0 + (i * kP16Threads + w_u0) / C::UPR, kv - 1);
+        ro = pl.row_offset(nb, n);
+      } else {
+        ro = rl.row_offset(n);
+      }
+      kpre[sl][i] = load16(k + ro + cu * 8);
+      vpre[sl][i] = load16(v + ro + cu * 8);
+      memory_order_point();
+    }
+  };
+  auto stash = [&](int buf, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
+    uint16_t* const k_lds = smem + buf * C::BUF;
+    uint16_t* const v_lds = k_lds + C::BN * C::RSE;
+#pragma unroll
+    for (int i = 0; i < C::UPT; ++i) {
+      const int u = i * kP16Threads + tid;
+      const int rr = u / C::UPR;
+      const int cu = u - rr * C::UPR;
+      *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[sl][i];
+      *reinterpret_cast<u32x4*>(v_lds + rr * C::RSV + cu * 8) = vpre[sl][i];
+    }
+  };
+
+  // V^T transpose reads: lane i of 16-lane group grp addresses key row 4*grp + i/4 (+16 for the
+  // second read) at d columns 4*(i%4) .. +3 of each 16-wide d tile.
+  const int tr_off = (4 * grp + ((lane & 15) >> 2)) * C::RSV + 4 * (lane & 3);
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, (C::PF > 1) ? 1 : 0>;
+  if (n_kt > 0) {
+    fetch(0, S0{});
+    stash(0, S0{});
+    fetch(C::BN, S1{});
+    if constexpr (C::PF > 1) fetch(2 * C::BN, S0{});
+  }
+  const int wave_first_row = m0 + w * 16;
+  const int wave_last_key = causal ? wave_first_row + 15 + off : 0x7fffffff;
+  auto step = [&](int t, auto slot_c) {
+    const int n0 = t * C::BN;
+    __syncthreads();  // tile t staged by every wave; tile t-1's buffer no longer read
+    const uint16_t* const k_lds = smem + (t & 1) * C::BUF;
+    const uint16_t* const v_lds = k_lds + C::BN * C::RSE;
+    if (n0 <= wave_last_key) {
+      f32x4 s[C::KT];
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt) s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < C::KT; ++kt) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+              k_lds + (kt * 16 + qcol) * C::RSE + ks * 32 + 8 * grp));
+          s[kt] = mfma16(a, qreg[ks], s[kt]);
+        }
+      const bool need_mask =
+          (n0 + C::BN > kv) || (causal && n0 + C::BN - 1 > wave_first_row + off);
+      if (need_mask) {
+        // key n0 + 16*kt + 4*grp + r is visible iff 16*kt + r <= thr
+        const int thr = lim - n0 - 4 * grp;
+#pragma unroll
+        for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kt + r > thr) s[kt][r] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][r]);
+      mx = max_xor32(max_xor16(mx));
+      const float tmax = mx * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleLog2) != 0) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= corr;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) o[dt] *= corr;
+      }
+      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+      float ps = 0.f;
+      bf16x8 pb[C::PS];
+#pragma unroll
+      for (int st = 0; st < C::PS; ++st) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float e =
+              fast_exp2(__builtin_fmaf(s[2 * st + (j >> 2)][j & 3], scale_log2, neg_m));
+          pv[j] = e;
+          ps += e;
+        }
+        pb[st] = pack_bf16x8(pv);
+      }
+      l_run += ps;
+#pragma unroll
+      for (int st = 0; st < C::PS; ++st)
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const uint16_t* vp = v_lds + st * 32 * C::RSV + dt * 16 + tr_off;
+          const u32x2 lo = lds_read_tr16(vp);
+          const u32x2 hi = lds_read_tr16(vp + 16 * C::RSV);
+          o[dt] = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[st], o[dt]);
+        }
+    }
+    // Unconditional, also after the last tile (a stage nobody reads, loads of clamped rows), so
+    // every path into the next step has issued the same loads.
+    stash((t + 1) & 1, slot_c);
+    fetch(n0 + (1 + C::PF) * C::BN, slot_c);
+  };
+  if (n_kt > 0) {
+    if constexpr (C::PF == 1) {
+      int t = 0;
+      do {
+        step(t, S0{});
+      } while (++t < n_kt);
+    } else {
+      for (int t = 0;; t += 2) {
+        step(t, S1{});
+        if (t + 1 >= n_kt) break;
+        step(t + 1, S0{});
+        if (t + 2 >= n_kt) break;
+      }
+    }
+  }
+
+  // normalise, stage the wave's 16 rows in LDS, then write whole rows with 16-byte stores
+  l_run = sum_xor32(sum_xor16(l_run));
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  __syncthreads();
+  uint16_t* const ost = smem + w * 16 * C::RSE;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    const int d = dt * 16 + 4 * grp;
+    *reinterpret_cast<u32x2*>(ost + qcol * C::RSE + d) =
+        u32x2{pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
+              pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = lane; u < 16 * C::UPR; u += kWave) {
+    const int rr = u / C::UPR;
+    const int cu = u - rr * C::UPR;
+    const int orow = wave_first_row + rr;
+    if (orow < qo)
+      store16(out + ((size_t)(q0 + orow) * Hq + h) * D + cu * 8,
+              *reinterpret_cast<const u32x4*>(ost + rr * C::RSE + cu * 8));
+  }
+}
+
+// head dims that run the 16-row form
+template <int D>
+constexpr bool use_p16() {
+#ifdef PKV_P16_ALL
+  return true;
+#else
+  return D >= 256;
+#endif
+}
+
 template <int D, bool PAGED>
 static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
   const int n_qt = (a.max_qo_len + kBM - 1) / kBM;
@@ -369,12 +639,20 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
   if (negate_q) scale_log2 = -scale_log2;
   if (!(scale_log2 >= 1.17549435e-38f)) scale_log2 = 1.17549435e-38f;  // zero (or denormal) scale
   const dim3 grid(a.num_q_heads, a.batch, n_qt);
-  hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(kPrefillThreads), 0, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
-                     a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
-                     a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads,
-                     a.block_size > 0 ? __builtin_ctz((unsigned)a.block_size) : 0);
+  const int bs_shift = a.block_size > 0 ? __builtin_ctz((unsigned)a.block_size) : 0;
+  if constexpr (use_p16<D>()) {
+    hipLaunchKernelGGL((prefill16_kernel<D, PAGED>), grid, dim3(kP16Threads), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
+                       a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
+                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads, bs_shift);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(kPrefillThreads), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
+                       a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
+                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads, bs_shift);
+  }
   return hipGetLastError();
 }
 
