@@ -52,9 +52,8 @@ struct PrefillCfg {
   static constexpr int UNITS = BN * UPR;            // units per tile (K or V)
   static constexpr int UPT = UNITS / kPrefillThreads;  // units per thread
   // kv tiles held in registers between their loads and their LDS stage: the loads of tile t+PF+1
-  // are issued while tile t is consumed. head_dim 256 runs one wave per SIMD, so nothing else
-  // hides its load latency: it keeps two tiles in flight.
-  static constexpr int PF = (D >= 256) ? 2 : 1;
+  // are issued while tile t is consumed (one tile of compute does not cover a load's latency).
+  static constexpr int PF = (D >= 128) ? 2 : 1;
   // two K+V tile buffers (double buffering), later reused for the output tile
   static constexpr int LDS_ELEMS = (2 * BUF > kBM * RSE) ? 2 * BUF : kBM * RSE;
   static_assert(UNITS % kPrefillThreads == 0, "tile units must divide evenly");
@@ -79,9 +78,9 @@ struct PagedLoader {
   __device__ __forceinline__ int block_of(int nb) const {
     return clampi(row[__builtin_amdgcn_readfirstlane(nb) >> bs_shift], 0, NB - 1);
   }
-  // row n lies in the same block as the wave-uniform row nb
-  __device__ __forceinline__ size_t row_offset(int nb, int n) const {
-    return (((size_t)block_of(nb) * Hkv + kh) * BS + (n & (BS - 1))) * D;
+  // first element of kv head kh in the block holding key nb
+  __device__ __forceinline__ size_t block_offset(int nb) const {
+    return ((size_t)block_of(nb) * Hkv + kh) * BS * D;
   }
 };
 
@@ -168,24 +167,30 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // Loads of tile rows n0 .. n0+BN-1; rows past the request's end re-read its last row (their
   // probabilities are exactly 0). Every call issues the same loads in the same order, whatever
   // n0 is, so the wait before each stage counts exactly the loads still needed.
+  const int last_n0 = (n_kt - 1) * C::BN;  // first row of the last tile
   auto fetch = [&](int n0, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
+    n0 = min(n0, last_n0);           // loads past the last tile repeat it
+    const int last_r = kv - 1 - n0;  // >= 0: the tile's last row inside the request
 #pragma unroll
     for (int i = 0; i < C::UPT; ++i) {
       const int u = i * kPrefillThreads + tid;
       const int rr = u / C::UPR;
       const int cu = u - rr * C::UPR;
-      const int n = min(n0 + rr, kv - 1);
-      size_t ro;
+      const int r = min(rr, last_r);
+      size_t base;  // wave-uniform
+      int off;      // per lane
       if constexpr (PAGED) {
         // the instruction's first row: wave-uniform, in the same block as every row it loads
         const int nb = min(n0 + (i * kPrefillThreads + w_u0) / C::UPR, kv - 1);
-        ro = pl.row_offset(nb, n);
+        base = pl.block_offset(nb);
+        off = ((n0 + r) & (BS - 1)) * D + cu * 8;
       } else {
-        ro = rl.row_offset(n);
+        base = rl.row_offset(n0);
+        off = r * (Hkv * D) + cu * 8;
       }
-      kpre[sl][i] = load16(k + ro + cu * 8);
-      vpre[sl][i] = load16(v + ro + cu * 8);
+      kpre[sl][i] = load16(k + base + off);
+      vpre[sl][i] = load16(v + base + off);
       memory_order_point();
     }
   };
@@ -456,24 +461,30 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // Loads of tile rows n0 .. n0+BN-1; rows past the request's end re-read its last row (their
   // probabilities are exactly 0). Every call issues the same loads in the same order, whatever
   // n0 is, so the wait before each stage counts exactly the loads still needed.
+  const int last_n0 = (n_kt - 1) * C::BN;  // first row of the last tile
   auto fetch = [&](int n0, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
+    n0 = min(n0, last_n0);           // loads past the last tile repeat it
+    const int last_r = kv - 1 - n0;  // >= 0: the tile's last row inside the request
 #pragma unroll
     for (int i = 0; i < C::UPT; ++i) {
       const int u = i * kP16Threads + tid;
       const int rr = u / C::UPR;
       const int cu = u - rr * C::UPR;
-      const int n = min(n0 + rr, kv - 1);
-      size_t ro;
+      const int r = min(rr, last_r);
+      size_t base;  // wave-uniform
+      int off;      // per lane
       if constexpr (PAGED) {
         // the instruction's first row: wave-uniform, in the same block as every row it loads
         const int nb = min(n0 + (i * kP16Threads + w_u0) / C::UPR, kv - 1);
-        ro = pl.row_offset(nb, n);
+        base = pl.block_offset(nb);
+        off = ((n0 + r) & (BS - 1)) * D + cu * 8;
       } else {
-        ro = rl.row_offset(n);
+        base = rl.row_offset(n0);
+        off = r * (Hkv * D) + cu * 8;
       }
-      kpre[sl][i] = load16(k + ro + cu * 8);
-      vpre[sl][i] = load16(v + ro + cu * 8);
+      kpre[sl][i] = load16(k + base + off);
+      vpre[sl][i] = load16(v + base + off);
       memory_order_point();
     }
   };
