@@ -21,7 +21,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_E_HIP; }
 // q-head group); when that is too few to fill 256 CUs several times over and sequences are
 // longer than one partition, split-KV with 512-token partitions (the vLLM page's _PARTITION_SIZE).
 constexpr int kDefaultPartition = 512;
-constexpr int kDirectMinGroups = 1024;
+constexpr int kDirectMinGroups = 512;  // two (sequence, kv head) work-groups per CU
 
 int resolve_partition(int batch, int num_q_heads, int num_kv_heads, int max_seq_len,
                       int partition_tokens) {

@@ -32,6 +32,7 @@ namespace pkv {
 constexpr int kDirectWaves = 4;  // waves per work-group on the direct path (split: one wave)
 constexpr float kRescaleLog2 = 8.0f;  // raise a running max only when exceeded by more than this
 constexpr int kPrefetch = 2;          // 32-token chunks per wave in flight (loads issued ahead)
+constexpr int kMergeUnroll = 8;       // merge: partial rows per thread in flight
 
 template <int D>
 struct DecodeCfg {
@@ -49,14 +50,6 @@ struct DecodeChunk {
   u32x4 v[2][DecodeCfg<D>::VU];
 };
 
-__device__ __forceinline__ float wave_max(float x) {
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
 
 // scale_log2 > 0 always: the host folds a negative scale into negate_q (an exact sign flip of q)
 // and replaces a zero scale by the smallest normal float (every probability is then exactly 1).
@@ -346,59 +339,87 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
   }
 }
 
-// Log-sum-exp merge of split partials: one work-group per (q head, sequence).
-template <int D>
-__global__ void __launch_bounds__(256)
+// Log-sum-exp merge of split partials: one work-group per (q head, sequence). Thread group g
+// (U threads, one float4 of the row each) folds partitions g, g+NG, ... into a running
+// (max, exp-sum, weighted output), loading kMergeUnroll partitions at a time; the NG group states
+// are then combined through LDS. One pass over the partials, all of a batch's loads in flight.
+template <int D, int NT>
+__global__ void __launch_bounds__(NT)
 decode_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ m_part,
                     const float* __restrict__ l_part, const int32_t* __restrict__ lens,
                     uint16_t* __restrict__ out, float* __restrict__ lse, int Hq, int max_blocks,
                     int BS, int PT, int Pmax) {
-  constexpr int U = D / 4;       // float4 units per partial row
-  constexpr int NG = 256 / U;    // partition groups
-  __shared__ float red[4];
-  __shared__ f32x4 red4[NG][U];
+  constexpr int U = D / 4;    // float4 units per partial row
+  constexpr int NG = NT / U;  // partition groups
+  __shared__ float sm[NG];
+  __shared__ float sl[NG];
+  __shared__ f32x4 so[NG][U];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int t = threadIdx.x;
   int L = clampi(lens[b], 0, max_blocks * BS);
   L = min(L, Pmax * PT);
-  const int P = (L + PT - 1) / PT;
+  const int P = (L + PT - 1) / PT;  // partitions holding tokens (each has a finite max)
   const size_t pi0 = ((size_t)b * Hq + h) * Pmax;
-
-  float M = -INFINITY;
-  for (int p = t; p < P; p += 256) M = fmaxf(M, m_part[pi0 + p]);
-  M = wave_max(M);
-  if ((t & 63) == 0) red[t >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float S = 0.f;
-  for (int p = t; p < P; p += 256) S += l_part[pi0 + p] * fast_exp2(m_part[pi0 + p] - M);
-  S = wave_sum(S);
-  if ((t & 63) == 0) red[t >> 6] = S;
-  __syncthreads();
-  S = red[0] + red[1] + red[2] + red[3];
-
   const int u = t % U;
   const int g = t / U;
+
+  float Mg = -INFINITY;  // log2 units
+  float Sg = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int p = g; p < P; p += NG) {
-    const float wgt = l_part[pi0 + p] * fast_exp2(m_part[pi0 + p] - M);
-    acc += wgt * reinterpret_cast<const f32x4*>(o_part + (pi0 + p) * D)[u];
-  }
-  red4[g][u] = acc;
-  __syncthreads();
-  if (g == 0) {
-    f32x4 sum = red4[0][u];
+  for (int p0 = g; p0 < P; p0 += NG * kMergeUnroll) {
+    f32x4 x[kMergeUnroll];
+    float mp[kMergeUnroll], lp[kMergeUnroll];
 #pragma unroll
-    for (int gg = 1; gg < NG; ++gg) sum += red4[gg][u];
-    const float inv = S > 0.f ? 1.f / S : 0.f;
-    sum *= inv;
-    *reinterpret_cast<u32x2*>(out + ((size_t)b * Hq + h) * D + u * 4) =
-        u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
-    if (lse != nullptr && u == 0)
-      lse[(size_t)b * Hq + h] = S > 0.f ? (M + __log2f(S)) * kLn2 : -INFINITY;
+    for (int j = 0; j < kMergeUnroll; ++j) {
+      const int p = p0 + j * NG;
+      x[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mp[j] = -INFINITY;
+      lp[j] = 0.f;
+      if (p < P) {
+        x[j] = reinterpret_cast<const f32x4*>(o_part + (pi0 + p) * D)[u];
+        mp[j] = m_part[pi0 + p];
+        lp[j] = l_part[pi0 + p];
+      }
+    }
+    float Mb = Mg;
+#pragma unroll
+    for (int j = 0; j < kMergeUnroll; ++j) Mb = fmaxf(Mb, mp[j]);
+    const float c = (Mg == -INFINITY) ? 0.f : fast_exp2(Mg - Mb);
+    acc *= c;
+    Sg *= c;
+#pragma unroll
+    for (int j = 0; j < kMergeUnroll; ++j) {
+      const float wj = (mp[j] == -INFINITY) ? 0.f : lp[j] * fast_exp2(mp[j] - Mb);
+      Sg += wj;
+      acc += wj * x[j];
+    }
+    Mg = Mb;
   }
+  if (u == 0) {
+    sm[g] = Mg;
+    sl[g] = Sg;
+  }
+  so[g][u] = acc;
+  __syncthreads();
+  if (g != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, sm[gg]);
+  float S = 0.f;
+  f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    const float c = (sm[gg] == -INFINITY) ? 0.f : fast_exp2(sm[gg] - M);
+    S += c * sl[gg];
+    sum += c * so[gg][u];
+  }
+  const float inv = S > 0.f ? 1.f / S : 0.f;
+  sum *= inv;
+  *reinterpret_cast<u32x2*>(out + ((size_t)b * Hq + h) * D + u * 4) =
+      u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+  if (lse != nullptr && u == 0)
+    lse[(size_t)b * Hq + h] = S > 0.f ? (M + __log2f(S)) * kLn2 : -INFINITY;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -435,10 +456,16 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
                        scale_log2, negate_q, __builtin_ctz((unsigned)a.block_size));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.num_q_heads, a.batch), dim3(256), 0,
-                       stream, a.o_part, a.m_part, a.l_part, a.seq_lens, (uint16_t*)a.out, a.lse,
-                       a.num_q_heads, a.max_blocks_per_seq, a.block_size, a.partition_tokens,
-                       a.max_partitions);
+    // long splits take 1024 threads per (head, sequence), so one batch of loads covers them
+    const dim3 mgrid(a.num_q_heads, a.batch);
+    if (a.max_partitions > 4 * kMergeUnroll)
+      hipLaunchKernelGGL((decode_merge_kernel<D, 1024>), mgrid, dim3(1024), 0, stream, a.o_part,
+                         a.m_part, a.l_part, a.seq_lens, (uint16_t*)a.out, a.lse, a.num_q_heads,
+                         a.max_blocks_per_seq, a.block_size, a.partition_tokens, a.max_partitions);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<D, 256>), mgrid, dim3(256), 0, stream, a.o_part,
+                         a.m_part, a.l_part, a.seq_lens, (uint16_t*)a.out, a.lse, a.num_q_heads,
+                         a.max_blocks_per_seq, a.block_size, a.partition_tokens, a.max_partitions);
     return hipGetLastError();
   }
   const dim3 grid(1, a.num_kv_heads * n_hg, a.batch);

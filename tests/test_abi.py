@@ -102,4 +102,9 @@ def test_workspace_bytes():
     al = lambda x: (x + 255) // 256 * 256
     want = al(B * Hq * P * D * 4) + 2 * al(B * Hq * P * 4)
     assert lib.pkv_decode_workspace_bytes(B, Hq, 8, D, L, 512) == want
-    assert lib.pkv_decode_workspace_bytes(B, Hq, 8, D, L, -1) == want
+    # library choice: direct from two (sequence, kv head) work-groups per CU (512) upwards, else
+    # split 512 when the context is longer than one partition
+    assert lib.pkv_decode_workspace_bytes(B, Hq, 8, D, L, -1) == 0
+    want_half = al(B // 2 * Hq * P * D * 4) + 2 * al(B // 2 * Hq * P * 4)
+    assert lib.pkv_decode_workspace_bytes(B // 2, Hq, 8, D, L, -1) == want_half
+    assert lib.pkv_decode_workspace_bytes(B // 2, Hq, 8, D, 512, -1) == 0
