@@ -257,7 +257,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const int hout = kh * G + gcol;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     if constexpr (SPLIT) {
-      const size_t pi = ((size_t)b * Hq + hout) * Pmax + p;
+      const size_t pi = ((size_t)b * Pmax + p) * Hq + hout;
       float* op = o_part + pi * D + 4 * qg;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) *reinterpret_cast<f32x4*>(op + mt * 16) = o[mt] * inv;
@@ -318,7 +318,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     }
     const int hout = kh * G + hg * 16 + oc;
     if constexpr (SPLIT) {
-      const size_t pi = ((size_t)b * Hq + hout) * Pmax + p;
+      const size_t pi = ((size_t)b * Pmax + p) * Hq + hout;
       float* op = o_part + pi * D + dpart * DPT;
 #pragma unroll
       for (int i = 0; i < DPT; i += 4)
@@ -360,7 +360,8 @@ decode_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ 
   int L = clampi(lens[b], 0, max_blocks * BS);
   L = min(L, Pmax * PT);
   const int P = (L + PT - 1) / PT;  // partitions holding tokens (each has a finite max)
-  const size_t pi0 = ((size_t)b * Hq + h) * Pmax;
+  // partial p of (b, h) is row (b * Pmax + p) * Hq + h
+  const size_t pi0 = (size_t)b * Pmax * Hq + h;
   const int u = t % U;
   const int g = t / U;
 
@@ -377,9 +378,10 @@ decode_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ 
       mp[j] = -INFINITY;
       lp[j] = 0.f;
       if (p < P) {
-        x[j] = reinterpret_cast<const f32x4*>(o_part + (pi0 + p) * D)[u];
-        mp[j] = m_part[pi0 + p];
-        lp[j] = l_part[pi0 + p];
+        const size_t pi = pi0 + (size_t)p * Hq;
+        x[j] = reinterpret_cast<const f32x4*>(o_part + pi * D)[u];
+        mp[j] = m_part[pi];
+        lp[j] = l_part[pi];
       }
     }
     float Mb = Mg;

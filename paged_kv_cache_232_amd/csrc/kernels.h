@@ -32,7 +32,7 @@ struct DecodeArgs {
   int max_partitions;
 };
 
-// Split-KV workspace layout for a given shape: o [B, Hq, P, D] f32, m and l [B, Hq, P] f32, each
+// Split-KV workspace layout for a given shape: o [B, P, Hq, D] f32, m and l [B, P, Hq] f32, each
 // region 256-byte aligned.
 struct DecodeWorkspaceLayout {
   size_t o_off, m_off, l_off, total;
