@@ -9,7 +9,9 @@ One step runs every call of the hot path once, on inputs already resident in HBM
   4. paged_attn_decode (split 512)        batch 4, 131072 tokens each, 64 q / 8 kv heads, hd 128
 Each call is bracketed by HIP events on the stream it is launched on. The headline value is the
 decode KV bandwidth (algorithmic bytes of calls 3 and 4 over their measured time); the ragged
-prefill TFLOP/s is reported beside it. The direct decode path of workload 3 is timed separately.
+prefill TFLOP/s is reported beside it. The direct and split decode paths of workload 3, and the
+block-management calls (copy_blocks over 32 layers, swap_blocks to pinned host memory), are timed
+separately, outside the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --calibrate-copy     (times a plain 1 GiB device copy, for counter scaling)
@@ -37,6 +39,7 @@ from workloads import CONFIGS, make_config  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0                          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # dense bf16 MFMA, 2516.6 TFLOP/s
+PCIE_PEAK_GBS = 64.0                           # PCIe 5.0 x16, one direction
 METRIC = "decode KV GB/s (% HBM peak); ragged-prefill bf16 TFLOP/s (% MFMA peak)"
 
 
@@ -112,7 +115,7 @@ class Case:
         self.ms = []
 
     def rate(self, ms):
-        return self.work / (ms * 1e-3) / (1e9 if self.kind == "hbm" else 1e12)
+        return self.work / (ms * 1e-3) / (1e12 if self.kind == "mfma" else 1e9)
 
 
 def build_cases(dev):
@@ -184,6 +187,24 @@ def build_cases(dev):
         meta[f"lens{cid}_sum"] = sum(lens)
         meta[f"flops{cid}"] = decode_flops(lens, Hq, D)
         del di
+    # block management around the cache (timed alone, outside the step): copy_blocks over 32
+    # layers of the batched-decode cache shape, and a swap-out of 256 blocks to pinned host memory
+    g = torch.Generator().manual_seed(232100)
+    nb, layers, npairs = 2048, 32, 256
+    blk_shape = (nb, 8, 16, 128)
+    kcs = [torch.empty(blk_shape, dtype=torch.bfloat16, device=dev).normal_() for _ in range(layers)]
+    vcs = [torch.empty(blk_shape, dtype=torch.bfloat16, device=dev).normal_() for _ in range(layers)]
+    perm = torch.randperm(nb, generator=g)
+    cmap = torch.stack([perm[:npairs], perm[npairs:2 * npairs]], 1).to(torch.int64).to(dev)
+    block_bytes = 8 * 16 * 128 * 2
+    cases["copy_blocks"] = Case(
+        f"copy_blocks ({layers} layers, {npairs} pairs, 32 KiB blocks, K and V)",
+        lambda: pkv.copy_blocks(kcs, vcs, cmap), "hbm", 2 * 2 * layers * npairs * block_bytes, "GB/s")
+    host = torch.empty((npairs,) + blk_shape[1:], dtype=torch.bfloat16, pin_memory=True)
+    smap = torch.stack([perm[:npairs], torch.arange(npairs)], 1).to(torch.int64)
+    cases["swap_out"] = Case(
+        f"swap_blocks device -> pinned host ({npairs} scattered 32 KiB blocks)",
+        lambda: pkv.swap_blocks(kcs[0], host, smap), "pcie", npairs * block_bytes, "GB/s")
     return cases, meta
 
 
@@ -310,20 +331,20 @@ def main():
     cases, meta = build_cases(dev)
     print("# inputs resident; timing", file=sys.stderr, flush=True)
     ms_step, wall = time_step(cases, args.steps, args.warmup)
-    for k in ("decode3_direct", "decode3_split"):
+    for k in ("decode3_direct", "decode3_split", "copy_blocks", "swap_out"):
         time_alone(cases[k])
 
     def summary(k):
         c = cases[k]
         avg = statistics.fmean(c.ms)
         med = statistics.median(c.ms)
-        peak = HBM_PEAK_GBS if c.kind == "hbm" else MFMA_BF16_PEAK_TFLOPS
+        peak = {"hbm": HBM_PEAK_GBS, "mfma": MFMA_BF16_PEAK_TFLOPS, "pcie": PCIE_PEAK_GBS}[c.kind]
         r = c.rate(avg)
         return {"call": c.name, "avg_ms": round(avg, 5), "median_ms": round(med, 5), "work": c.work,
                 "rate": round(r, 2), "unit": c.unit, "frac_of_peak": round(r / peak, 4),
                 "hbm_traffic_bytes": measured_traffic(k)}
 
-    per = {k: summary(k) for k in STEP + ["decode3_direct", "decode3_split"]}
+    per = {k: summary(k) for k in STEP + ["decode3_direct", "decode3_split", "copy_blocks", "swap_out"]}
     dec_ms = sum(statistics.fmean(cases[k].ms) for k in ("decode3", "decode4"))
     dec_bytes = cases["decode3"].work + cases["decode4"].work
     value = dec_bytes / (dec_ms * 1e-3) / 1e9

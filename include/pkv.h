@@ -144,6 +144,42 @@ int pkv_validate_block_tables_h(const int32_t* block_tables_h, const int32_t* se
                                 int32_t batch, int32_t max_blocks_per_seq, int32_t block_size,
                                 int32_t num_blocks);
 
+/*
+ * copy_blocks — copy whole cache blocks inside every layer's key and value caches.
+ * Defined by the vLLM-derived paged_attn.py page, PagedAttention.copy_blocks: for each layer and
+ * each (src, dst) pair of the mapping, block dst of the layer's K cache becomes a copy of its block
+ * src, and the same for the V cache. A block is the contiguous [num_kv_heads, block_size, head_dim]
+ * run of the cache layout above.
+ *
+ *   k_cache_ptrs, v_cache_ptrs  DEVICE arrays [num_layers] of uint64 device addresses, one cache of
+ *                  num_blocks blocks per layer (16-byte aligned).
+ *   block_mapping  DEVICE int64 [num_pairs, 2]: (src block, dst block).
+ *   block_bytes    bytes of one block of one cache (a multiple of 16).
+ * Pairs naming a block outside [0, num_blocks) are skipped on the device. Destination blocks must
+ * be distinct and must not be the source of another pair (else the result is unspecified).
+ * num_layers == 0 or num_pairs == 0 is a no-op.
+ */
+int pkv_copy_blocks(const uint64_t* k_cache_ptrs, const uint64_t* v_cache_ptrs, int32_t num_layers,
+                    const int64_t* block_mapping, int32_t num_pairs, int64_t block_bytes,
+                    int32_t num_blocks, void* stream);
+
+/*
+ * swap_blocks — copy whole blocks from one cache to another that may live in another memory
+ * (device and host), as the vLLM-derived paged_attn.py page's PagedAttention.swap_blocks does when
+ * blocks are swapped out to, or in from, host memory. Call once per cache (K, then V).
+ *
+ *   src, dst         caches of src_num_blocks / dst_num_blocks blocks; device or host memory
+ *                    (pinned host memory keeps the copies asynchronous on `stream`).
+ *   block_mapping_h  HOST int64 [num_pairs, 2]: (src block, dst block), checked on the host.
+ * When the GPU can address both caches (device memory, pinned host memory) one kernel moves every
+ * block (block_bytes a multiple of 16); otherwise HIP copies move each run of pairs whose source and
+ * destination blocks both advance by one. Destination blocks must be distinct.
+ * PKV_E_INVALID_ARGUMENT for a block index out of range (before any copy is enqueued).
+ */
+int pkv_swap_blocks(const void* src, void* dst, const int64_t* block_mapping_h, int32_t num_pairs,
+                    int64_t block_bytes, int32_t src_num_blocks, int32_t dst_num_blocks,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,3 +25,4 @@ from .attention import (  # noqa: F401
     validate_block_tables,
     STATUS,
 )
+from .blocks import copy_blocks, swap_blocks  # noqa: F401,E402

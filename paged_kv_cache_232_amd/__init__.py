@@ -26,6 +26,7 @@ _c_i32 = ctypes.c_int32
 _c_ptr = ctypes.c_void_p
 _c_f32 = ctypes.c_float
 _c_size = ctypes.c_size_t
+_c_i64 = ctypes.c_int64
 
 # name -> (restype, argtypes)
 _SIGNATURES = {
@@ -43,6 +44,8 @@ _SIGNATURES = {
                                          _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                          _c_i32, _c_i32, _c_i32, _c_f32, _c_ptr]),
     "pkv_validate_block_tables_h": (ctypes.c_int, [_c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_copy_blocks": (ctypes.c_int, [_c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i64, _c_i32, _c_ptr]),
+    "pkv_swap_blocks": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i64, _c_i32, _c_i32, _c_ptr]),
 }
 
 _lib = None
@@ -251,3 +254,58 @@ def validate_block_tables(block_tables, seq_lens, block_size: int, num_blocks: i
     return int(load_library().pkv_validate_block_tables_h(
         ctypes.c_void_p(t.data_ptr()) if t.numel() else None, ctypes.c_void_p(lens.data_ptr()) if B else None,
         B, width, int(block_size), int(num_blocks)))
+
+
+def _block_bytes(cache: torch.Tensor) -> int:
+    return cache[0].numel() * cache.element_size() if cache.shape[0] else 0
+
+
+def copy_blocks(k_caches, v_caches, block_mapping: torch.Tensor) -> None:
+    """Copy whole blocks inside every layer's caches: for each (src, dst) row of block_mapping
+    [n, 2] (int64, on the caches' device), block dst of each K and V cache becomes a copy of block src.
+    k_caches / v_caches: lists (one per layer) of caches [NB, Hkv, BS, D] of one shape and dtype."""
+    lib = load_library()
+    k_caches, v_caches = list(k_caches), list(v_caches)
+    if len(k_caches) != len(v_caches):
+        raise ValueError("one K and one V cache per layer")
+    if not k_caches:
+        return
+    ref = k_caches[0]
+    dev = ref.device
+    for c in k_caches + v_caches:
+        _need(c, "cache", ref.dtype, ref.dim(), dev)
+        if c.shape != ref.shape:
+            raise ValueError("every cache must have the same shape")
+        if c.data_ptr() % 16:
+            raise ValueError("caches must be 16-byte aligned")
+    _need(block_mapping, "block_mapping", torch.int64, 2, dev)
+    if block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [n, 2]")
+    kp = torch.tensor([c.data_ptr() for c in k_caches], dtype=torch.int64).to(dev)
+    vp = torch.tensor([c.data_ptr() for c in v_caches], dtype=torch.int64).to(dev)
+    _check(lib.pkv_copy_blocks(_ptr(kp), _ptr(vp), len(k_caches), _ptr(block_mapping), block_mapping.shape[0],
+                               _block_bytes(ref), ref.shape[0], _stream(ref)), "copy_blocks")
+    # kp / vp may be freed on return: the caching allocator reuses their memory only for work
+    # ordered after this launch on the same stream
+
+
+def swap_blocks(src: torch.Tensor, dst: torch.Tensor, block_mapping) -> None:
+    """Copy whole blocks from cache src to cache dst (device or host memory, same block shape):
+    for each (src, dst) row of block_mapping [n, 2] (int64, host), dst[d] = src[s]. Call per cache."""
+    lib = load_library()
+    if src.dtype != dst.dtype or src.shape[1:] != dst.shape[1:]:
+        raise ValueError("src and dst must have the same block shape and dtype")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    m = block_mapping.detach().to("cpu", torch.int64).contiguous() if isinstance(block_mapping, torch.Tensor) \
+        else torch.tensor(block_mapping, dtype=torch.int64)
+    if m.dim() != 2 or m.shape[1] != 2:
+        raise ValueError("block_mapping must be [n, 2]")
+    dev_t = src if src.is_cuda else dst
+    if not dev_t.is_cuda:
+        raise ValueError("one of src / dst must be a device tensor")
+    _check(lib.pkv_swap_blocks(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                               ctypes.c_void_p(m.data_ptr()) if m.numel() else None, m.shape[0],
+                               _block_bytes(src) if src.shape[0] else _block_bytes(dst), src.shape[0],
+                               dst.shape[0], _stream(dev_t)), "swap_blocks")
+

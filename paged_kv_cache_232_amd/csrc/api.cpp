@@ -254,4 +254,32 @@ int pkv_validate_block_tables_h(const int32_t* block_tables_h, const int32_t* se
   return PKV_OK;
 }
 
+int pkv_copy_blocks(const uint64_t* k_cache_ptrs, const uint64_t* v_cache_ptrs, int32_t num_layers,
+                    const int64_t* block_mapping, int32_t num_pairs, int64_t block_bytes,
+                    int32_t num_blocks, void* stream) {
+  if (num_layers < 0 || num_pairs < 0 || num_blocks < 0 || block_bytes <= 0 || block_bytes % 16 != 0)
+    return PKV_E_INVALID_ARGUMENT;
+  if (num_layers == 0 || num_pairs == 0) return PKV_OK;
+  if (!k_cache_ptrs || !v_cache_ptrs || !block_mapping) return PKV_E_INVALID_ARGUMENT;
+  if (num_layers > 65535) return PKV_E_INVALID_ARGUMENT;  // grid y limit
+  return hip_status(pkv::launch_copy_blocks(k_cache_ptrs, v_cache_ptrs, num_layers, block_mapping,
+                                            num_pairs, block_bytes, num_blocks,
+                                            (hipStream_t)stream));
+}
+
+int pkv_swap_blocks(const void* src, void* dst, const int64_t* block_mapping_h, int32_t num_pairs,
+                    int64_t block_bytes, int32_t src_num_blocks, int32_t dst_num_blocks,
+                    void* stream) {
+  if (num_pairs < 0 || block_bytes <= 0 || src_num_blocks < 0 || dst_num_blocks < 0)
+    return PKV_E_INVALID_ARGUMENT;
+  if (num_pairs == 0) return PKV_OK;
+  if (!src || !dst || !block_mapping_h) return PKV_E_INVALID_ARGUMENT;
+  for (int i = 0; i < num_pairs; ++i) {
+    const int64_t s = block_mapping_h[2 * i], d = block_mapping_h[2 * i + 1];
+    if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks) return PKV_E_INVALID_ARGUMENT;
+  }
+  return hip_status(pkv::swap_blocks(src, dst, block_mapping_h, num_pairs, block_bytes,
+                                     (hipStream_t)stream));
+}
+
 }  // extern "C"

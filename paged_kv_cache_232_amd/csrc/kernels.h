@@ -62,6 +62,12 @@ struct PrefillArgs {
 };
 
 hipError_t launch_ragged_prefill(const PrefillArgs& a, hipStream_t stream);
+
+hipError_t launch_copy_blocks(const uint64_t* k_ptrs, const uint64_t* v_ptrs, int num_layers,
+                              const int64_t* mapping, int num_pairs, int64_t block_bytes,
+                              int num_blocks, hipStream_t stream);
+hipError_t swap_blocks(const void* src, void* dst, const int64_t* mapping_h, int num_pairs,
+                       int64_t block_bytes, hipStream_t stream);
 hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace pkv

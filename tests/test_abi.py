@@ -24,7 +24,7 @@ def _declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = pkv.load_library()
     syms = _declared_symbols()
-    assert len(syms) == 7, syms
+    assert len(syms) == 9, syms
     for s in syms:
         assert hasattr(lib, s), f"{s} missing from libpkv.so"
     assert set(syms) == set(pkv._SIGNATURES), "binding and header disagree"
@@ -108,3 +108,21 @@ def test_workspace_bytes():
     want_half = al(B // 2 * Hq * P * D * 4) + 2 * al(B // 2 * Hq * P * 4)
     assert lib.pkv_decode_workspace_bytes(B // 2, Hq, 8, D, L, -1) == want_half
     assert lib.pkv_decode_workspace_bytes(B // 2, Hq, 8, D, 512, -1) == 0
+
+
+def test_block_calls_argument_errors():
+    lib = pkv.load_library()
+    nul = None
+    fake = ctypes.c_void_p(16)
+    # copy_blocks: bad sizes are rejected; empty work is a no-op that touches no pointer
+    assert lib.pkv_copy_blocks(fake, fake, 1, fake, 1, 100, 4, nul) == pkv.E_INVALID_ARGUMENT  # not x16
+    assert lib.pkv_copy_blocks(fake, fake, -1, fake, 1, 64, 4, nul) == pkv.E_INVALID_ARGUMENT
+    assert lib.pkv_copy_blocks(nul, nul, 0, nul, 5, 64, 4, nul) == pkv.OK
+    assert lib.pkv_copy_blocks(nul, nul, 2, nul, 0, 64, 4, nul) == pkv.OK
+    assert lib.pkv_copy_blocks(nul, fake, 2, fake, 3, 64, 4, nul) == pkv.E_INVALID_ARGUMENT
+    # swap_blocks: the host mapping is checked before any copy is enqueued
+    m = np.array([[0, 1], [5, 0]], dtype=np.int64)
+    mp = m.ctypes.data_as(ctypes.c_void_p)
+    assert lib.pkv_swap_blocks(fake, fake, mp, 2, 64, 4, 4, nul) == pkv.E_INVALID_ARGUMENT
+    assert lib.pkv_swap_blocks(fake, fake, mp, 2, 0, 8, 8, nul) == pkv.E_INVALID_ARGUMENT
+    assert lib.pkv_swap_blocks(nul, nul, nul, 0, 64, 4, 4, nul) == pkv.OK

@@ -457,3 +457,72 @@ def test_planted_gather_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(A, "gather_tokens", wrong)
     with pytest.raises(AssertionError):
         test_golden_decode_gqa_shuffled_table()
+
+
+# ----------------------------------------------------------------------------------------------
+# Block management: copy_blocks / swap_blocks
+# ----------------------------------------------------------------------------------------------
+def _golden_blocks():
+    import json, os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "copy_blocks.json")) as f:
+        return json.load(f)
+
+
+def test_golden_copy_and_swap_blocks():
+    g = _golden_blocks()
+    kc = np.array(g["k_cache"], dtype=np.int16)
+    vc = np.array(g["v_cache"], dtype=np.int16)
+    (k2,), (v2,) = oracle.copy_blocks([kc], [vc], g["mapping"])
+    np.testing.assert_array_equal(k2, np.array(g["k_after"], dtype=np.int16))
+    np.testing.assert_array_equal(v2, np.array(g["v_after"], dtype=np.int16))
+    out = oracle.swap_blocks(kc, np.array(g["swap_dst"], dtype=np.int16), g["swap_mapping"])
+    np.testing.assert_array_equal(out, np.array(g["swap_after"], dtype=np.int16))
+
+
+def test_copy_blocks_invariants():
+    rng = np.random.default_rng(7)
+    layers = [rng.integers(-30000, 30000, size=(12, 2, 4, 8), dtype=np.int16) for _ in range(3)]
+    vals = [rng.integers(-30000, 30000, size=(12, 2, 4, 8), dtype=np.int16) for _ in range(3)]
+    m = np.array([[1, 5], [2, 7], [9, 0]])
+    ks, vs = oracle.copy_blocks(layers, vals, m)
+    for l in range(3):
+        for s, d in m:
+            np.testing.assert_array_equal(ks[l][d], layers[l][s])
+            np.testing.assert_array_equal(vs[l][d], vals[l][s])
+        untouched = [b for b in range(12) if b not in m[:, 1]]
+        np.testing.assert_array_equal(ks[l][untouched], layers[l][untouched])
+    # the pairs act at once: any order of the rows gives the same caches
+    ks2, _ = oracle.copy_blocks(layers, vals, m[::-1])
+    for a, b in zip(ks, ks2):
+        np.testing.assert_array_equal(a, b)
+    # out-of-range pairs are skipped, identity pairs change nothing
+    ks3, _ = oracle.copy_blocks(layers, vals, [[3, 3], [40, 1], [-1, 2], [1, 99]])
+    for a, b in zip(ks3, layers):
+        np.testing.assert_array_equal(a, b)
+    with pytest.raises(ValueError):
+        oracle.copy_blocks(layers, vals, [[1, 2], [3, 2]])
+    with pytest.raises(ValueError):
+        oracle.copy_blocks(layers, vals, [[1, 2], [2, 3]])
+
+
+def test_swap_blocks_round_trip():
+    rng = np.random.default_rng(8)
+    dev = rng.integers(-30000, 30000, size=(10, 2, 16, 8), dtype=np.int16)
+    host = np.zeros((6, 2, 16, 8), dtype=np.int16)
+    out_map = np.array([[7, 0], [2, 1], [3, 2], [4, 3]])
+    host2 = oracle.swap_blocks(dev, host, out_map)
+    back = oracle.swap_blocks(host2, np.zeros_like(dev), out_map[:, ::-1])
+    np.testing.assert_array_equal(back[out_map[:, 0]], dev[out_map[:, 0]])
+    np.testing.assert_array_equal(host2[4:], host[4:])
+    with pytest.raises(IndexError):
+        oracle.swap_blocks(dev, host, [[10, 0]])
+
+
+def test_planted_copy_direction_mistake_is_caught(monkeypatch):
+    g = _golden_blocks()
+    kc = np.array(g["k_cache"], dtype=np.int16)
+    vc = np.array(g["v_cache"], dtype=np.int16)
+    real = oracle.blocks._pairs
+    monkeypatch.setattr(oracle.blocks, "_pairs", lambda m: real(m)[:, ::-1])
+    (k2,), _ = oracle.copy_blocks([kc], [vc], g["mapping"])
+    assert not np.array_equal(k2, np.array(g["k_after"], dtype=np.int16))
