@@ -526,3 +526,101 @@ def test_planted_copy_direction_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(oracle.blocks, "_pairs", lambda m: real(m)[:, ::-1])
     (k2,), _ = oracle.copy_blocks([kc], [vc], g["mapping"])
     assert not np.array_equal(k2, np.array(g["k_after"], dtype=np.int16))
+
+
+# ----------------------------------------------------------------------------------------------
+# FP8 (e4m3) cache: the format's definition pinned by its special values, ties and error bound
+# ----------------------------------------------------------------------------------------------
+def test_e4m3_special_values():
+    v = oracle.e4m3_value
+    assert v(0x38) == 1.0 and v(0xB8) == -1.0
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0
+    assert v(0x01) == 2.0 ** -9 and v(0x07) == 7 * 2.0 ** -9 and v(0x08) == 2.0 ** -6
+    assert v(0x00) == 0.0 and np.signbit(v(0x80))
+    assert np.isnan(v(0x7F)) and np.isnan(v(0xFF))
+    assert v(0x3F) == 1.875 and v(0x40) == 2.0
+    # exactly 254 finite codes, 126 distinct positive magnitudes
+    finite = [c for c in range(256) if not np.isnan(v(c))]
+    assert len(finite) == 254
+
+
+def test_e4m3_round_trip_and_monotonic():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes).astype(np.float32)
+    np.testing.assert_array_equal(oracle.e4m3_encode(vals), codes)
+    x = np.linspace(-500, 500, 20001, dtype=np.float32)
+    dec = oracle.e4m3_decode(oracle.e4m3_encode(x))
+    assert np.all(np.diff(dec) >= 0)
+
+
+def test_e4m3_ties_saturation_and_nan():
+    enc = oracle.e4m3_encode
+    # midpoints go to the even code, anything off the midpoint to the nearer code
+    pos = oracle.e4m3_decode(np.arange(0x7F))
+    for c in range(0x7E):
+        mid = (pos[c] + pos[c + 1]) / 2
+        if np.float32(mid) != mid:
+            continue
+        want = c if c % 2 == 0 else c + 1
+        assert enc(np.float32(mid))[()] == want, hex(c)
+        assert enc(np.nextafter(np.float32(mid), np.float32(0)))[()] == c
+        assert enc(np.nextafter(np.float32(mid), np.float32(1e9)))[()] == c + 1
+    np.testing.assert_array_equal(enc(np.array([448, 449, 1e30, np.inf, -np.inf, -600], dtype=np.float32)),
+                                  [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE])
+    np.testing.assert_array_equal(enc(np.array([np.nan, -np.nan], dtype=np.float32)), [0x7F, 0x7F])
+    np.testing.assert_array_equal(enc(np.array([-0.0, 0.0], dtype=np.float32)), [0x80, 0x00])
+
+
+def test_fp8_quantize_error_bound():
+    # round to nearest: the error is at most half the spacing of the codes around x
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(50000) * 40).astype(np.float32)
+    scale = 0.37
+    y = (x / np.float32(scale)).astype(np.float64)
+    back = oracle.e4m3_decode(oracle.quantize(x, scale))
+    err = np.abs(back - np.clip(y, -448, 448))
+    a = np.abs(np.clip(y, -448, 448))
+    spacing = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+    assert np.all(err <= spacing / 2 + 1e-12)
+
+
+def test_fp8_decode_equals_bf16_decode_on_exact_values():
+    # integer-valued K and V in [-8, 8] are exact in both formats: with unit scales the fp8 path is
+    # the bf16 path
+    import torch
+    g = torch.Generator().manual_seed(3)
+    B, Hq, Hkv, D, bs, nb = 2, 4, 2, 64, 16, 12
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kc = torch.randint(-8, 9, (nb, Hkv, bs, D), generator=g).to(torch.bfloat16)
+    vc = torch.randint(-8, 9, (nb, Hkv, bs, D), generator=g).to(torch.bfloat16)
+    tables = torch.tensor([[3, 7, 1, 0], [5, 2, 9, 11]], dtype=torch.int32)
+    lens = torch.tensor([50, 33], dtype=torch.int32)
+    kq, vq = oracle.quantize(kc, 1.0), oracle.quantize(vc, 1.0)
+    ref = oracle.paged_decode(q, kc, vc, tables, lens, 0.125)
+    got = oracle.paged_decode_fp8(q, kq, vq, tables, lens, 0.125, 1.0, 1.0)
+    np.testing.assert_array_equal(ref, got)
+    # scales apply to the stored values: k_scale 2 with codes of kc/2 is the same cache
+    kq2 = oracle.quantize(kc, 2.0)
+    got2 = oracle.paged_decode_fp8(q, kq2, vq, tables, lens, 0.125, 2.0, 1.0)
+    np.testing.assert_allclose(ref, got2, rtol=0, atol=1e-12)
+
+
+def test_fp8_scatter_matches_quantized_bf16_scatter():
+    import torch
+    g = torch.Generator().manual_seed(4)
+    T, Hkv, D, bs, nb = 9, 2, 64, 16, 4
+    k = torch.randn(T, Hkv, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(T, Hkv, D, generator=g).to(torch.bfloat16)
+    slots = torch.tensor([0, 17, 5, -1, 63, 40, 41, 2, 30], dtype=torch.int64)
+    kc0 = torch.zeros(nb, Hkv, bs, D, dtype=torch.uint8)
+    vc0 = torch.zeros(nb, Hkv, bs, D, dtype=torch.uint8)
+    kc, vc = oracle.reshape_and_cache_fp8(k, v, kc0, vc0, slots, 0.5, 0.25)
+    for t, s in enumerate(slots.tolist()):
+        if s < 0:
+            continue
+        np.testing.assert_array_equal(kc[s // bs, :, s % bs], oracle.quantize(k[t], 0.5))
+        np.testing.assert_array_equal(vc[s // bs, :, s % bs], oracle.quantize(v[t], 0.25))
+    written = {s for s in slots.tolist() if s >= 0}
+    for s in range(nb * bs):
+        if s not in written:
+            assert not kc[s // bs, :, s % bs].any()
