@@ -9,9 +9,9 @@ One step runs every call of the hot path once, on inputs already resident in HBM
   4. paged_attn_decode (split 512)        batch 4, 131072 tokens each, 64 q / 8 kv heads, hd 128
 Each call is bracketed by HIP events on the stream it is launched on. The headline value is the
 decode KV bandwidth (algorithmic bytes of calls 3 and 4 over their measured time); the ragged
-prefill TFLOP/s is reported beside it. The direct and split decode paths of workload 3, and the
-block-management calls (copy_blocks over 32 layers, swap_blocks to pinned host memory), are timed
-separately, outside the step.
+prefill TFLOP/s is reported beside it. The direct and split decode paths of workload 3, decode of
+workloads 3 and 4 over an fp8 (e4m3) cache, and the block-management calls (copy_blocks over 32
+layers, swap_blocks to pinned host memory) are timed separately, outside the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --calibrate-copy     (times a plain 1 GiB device copy, for counter scaling)
@@ -83,6 +83,11 @@ def decode_bytes(lens, hq, hkv, d, bs) -> int:
     qo = 2 * len(lens) * hq * d * 2
     table = sum((L + bs - 1) // bs for L in lens) * 4 + 4 * len(lens)
     return kv + qo + table
+
+
+def decode_bytes_fp8(lens, hq, hkv, d, bs) -> int:
+    """As decode_bytes with one byte per cached K / V element (fp8 e4m3 codes)."""
+    return decode_bytes(lens, hq, hkv, d, bs) - sum(2 * L * hkv * d for L in lens)
 
 
 def decode_flops(lens, hq, d) -> int:
@@ -184,6 +189,18 @@ def build_cases(dev):
                                            "GB/s")
             cases["decode3_split"] = Case("paged_attn_decode split 512 (batched decode)", mk(c, 512), "hbm", work,
                                           "GB/s")
+        # the same workload over an fp8 (e4m3) cache (timed alone): codes of cache / scale, one byte
+        # per element, so half the bytes of the bf16 cache
+        c["k_scale"], c["v_scale"] = 0.02, 0.02
+        c["kc8"] = (c["kc"].float() / c["k_scale"]).to(torch.float8_e4m3fn).view(torch.uint8)
+        c["vc8"] = (c["vc"].float() / c["v_scale"]).to(torch.float8_e4m3fn).view(torch.uint8)
+
+        def mk8(c=c, pt=pt):
+            return lambda: pkv.paged_attn_decode(c["q"], c["kc8"], c["vc8"], c["bt"], c["sl"], c["scale"],
+                                                 max_seq_len=c["msl"], partition_tokens=pt, out=c["out"],
+                                                 workspace=c["ws"], k_scale=c["k_scale"], v_scale=c["v_scale"])
+        cases[key + "_fp8"] = Case(f"paged_attn_decode_fp8 ({CONFIGS[cid]['name']} over an e4m3 cache)", mk8(),
+                                   "hbm", decode_bytes_fp8(lens, Hq, Hkv, D, di.block_size), "GB/s")
         meta[f"lens{cid}_sum"] = sum(lens)
         meta[f"flops{cid}"] = decode_flops(lens, Hq, D)
         del di
@@ -209,6 +226,8 @@ def build_cases(dev):
 
 
 STEP = ["scatter5", "paged5", "ragged2", "decode3", "decode4"]
+# timed alone, outside the step
+EXTRA = ["decode3_direct", "decode3_split", "decode3_fp8", "decode4_fp8", "copy_blocks", "swap_out"]
 
 
 def time_step(cases, steps, warmup):
@@ -331,7 +350,7 @@ def main():
     cases, meta = build_cases(dev)
     print("# inputs resident; timing", file=sys.stderr, flush=True)
     ms_step, wall = time_step(cases, args.steps, args.warmup)
-    for k in ("decode3_direct", "decode3_split", "copy_blocks", "swap_out"):
+    for k in EXTRA:
         time_alone(cases[k])
 
     def summary(k):
@@ -344,7 +363,7 @@ def main():
                 "rate": round(r, 2), "unit": c.unit, "frac_of_peak": round(r / peak, 4),
                 "hbm_traffic_bytes": measured_traffic(k)}
 
-    per = {k: summary(k) for k in STEP + ["decode3_direct", "decode3_split", "copy_blocks", "swap_out"]}
+    per = {k: summary(k) for k in STEP + EXTRA}
     dec_ms = sum(statistics.fmean(cases[k].ms) for k in ("decode3", "decode4"))
     dec_bytes = cases["decode3"].work + cases["decode4"].work
     value = dec_bytes / (dec_ms * 1e-3) / 1e9

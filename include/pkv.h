@@ -145,6 +145,34 @@ int pkv_validate_block_tables_h(const int32_t* block_tables_h, const int32_t* se
                                 int32_t num_blocks);
 
 /*
+ * FP8 KV cache. The vLLM-derived paged_attn.py page passes kv_cache_dtype with per-tensor k_scale
+ * and v_scale floats to write_to_paged_cache and forward_decode. Here the fp8 cache holds OCP FP8
+ * E4M3 codes (bias 7, no infinities, max 448, S.1111.111 = NaN) in the same
+ * [num_blocks, num_kv_heads, block_size, head_dim] layout, one byte per element:
+ *   stored code = e4m3(x / scale): x the bf16 input in fp32, IEEE fp32 division, round to nearest
+ *                 even, magnitudes beyond 448 saturate to 448, NaN stored as 0x7F;
+ *   read value  = decode(code) * scale.
+ * k_scale and v_scale must be finite and > 0 (else PKV_E_INVALID_ARGUMENT).
+ */
+
+/* reshape_and_cache into an fp8 cache: as pkv_reshape_and_cache (same slot rules), storing the
+ * codes of k / k_scale and v / v_scale. head_dim a multiple of 16. Bit-exact. */
+int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks, float k_scale,
+                              float v_scale, void* stream);
+
+/* paged_attn_decode over an fp8 cache: as pkv_paged_attn_decode (same arguments, paths, workspace
+ * and output), with K = decode(code) * k_scale and V = decode(code) * v_scale. */
+int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                              float* lse, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                              float k_scale, float v_scale, int32_t partition_tokens,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * copy_blocks — copy whole cache blocks inside every layer's key and value caches.
  * Defined by the vLLM-derived paged_attn.py page, PagedAttention.copy_blocks: for each layer and
  * each (src, dst) pair of the mapping, block dst of the layer's K cache becomes a copy of its block

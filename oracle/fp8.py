@@ -62,32 +62,20 @@ def e4m3_decode(codes) -> np.ndarray:
 def e4m3_encode(x) -> np.ndarray:
     """fp32 values -> e4m3 codes (uint8): nearest representable magnitude, ties to the even
     mantissa (even code), saturation at 448, sign kept (zero included), NaN -> 0x7F."""
-    x = np.asarray(x, dtype=np.float32).astype(np.float64)
-    out = np.empty(x.shape, dtype=np.uint8)
-    flat_x, flat_o = x.reshape(-1), out.reshape(-1)
-    for i, v in enumerate(flat_x):
-        if np.isnan(v):
-            flat_o[i] = 0x7F
-            continue
-        sign = 0x80 if np.signbit(v) else 0x00
-        a = abs(v)
-        if a >= E4M3_MAX:
-            flat_o[i] = sign | 0x7E
-            continue
-        j = int(np.searchsorted(_POS_VALUES, a))  # _POS_VALUES[j-1] < a <= _POS_VALUES[j]
-        if j < len(_POS_VALUES) and _POS_VALUES[j] == a:
-            c = j
-        else:
-            lo, hi = j - 1, j
-            dlo, dhi = a - _POS_VALUES[lo], _POS_VALUES[hi] - a
-            if dlo < dhi:
-                c = lo
-            elif dhi < dlo:
-                c = hi
-            else:
-                c = lo if lo % 2 == 0 else hi  # tie: the even code has the even mantissa
-        flat_o[i] = sign | _POS_CODES[c]
-    return out
+    v = np.asarray(x, dtype=np.float32).astype(np.float64)
+    nan = np.isnan(v)
+    sign = np.signbit(v)
+    a = np.where(nan, 0.0, np.abs(v))
+    # neighbours in the ordered table of magnitudes: vals[lo] <= a <= vals[hi]
+    hi = np.clip(np.searchsorted(_POS_VALUES, a), 1, len(_POS_VALUES) - 1)
+    lo = hi - 1
+    dlo = a - _POS_VALUES[lo]
+    dhi = _POS_VALUES[hi] - a
+    tie_pick = np.where(lo % 2 == 0, lo, hi)  # the even code has the even mantissa
+    c = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, tie_pick))
+    c = np.where(a >= E4M3_MAX, 0x7E, c)
+    codes = (c | np.where(sign, 0x80, 0)).astype(np.uint8)
+    return np.where(nan, np.uint8(0x7F), codes).astype(np.uint8)
 
 
 def quantize(x, scale: float) -> np.ndarray:

@@ -44,6 +44,12 @@ _SIGNATURES = {
                                          _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                          _c_i32, _c_i32, _c_i32, _c_f32, _c_ptr]),
     "pkv_validate_block_tables_h": (ctypes.c_int, [_c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_reshape_and_cache_fp8": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32,
+                                                 _c_i32, _c_i32, _c_i32, _c_f32, _c_f32, _c_ptr]),
+    "pkv_paged_attn_decode_fp8": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                 _c_i32, _c_f32, _c_f32, _c_f32, _c_i32, _c_ptr, _c_size,
+                                                 _c_ptr]),
     "pkv_copy_blocks": (ctypes.c_int, [_c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i64, _c_i32, _c_ptr]),
     "pkv_swap_blocks": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i64, _c_i32, _c_i32, _c_ptr]),
 }
@@ -140,15 +146,21 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, *,
                       max_seq_len: Optional[int] = None, partition_tokens: int = -1,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      workspace: Optional[torch.Tensor] = None, k_scale: Optional[float] = None,
+                      v_scale: Optional[float] = None) -> torch.Tensor:
     """Decode attention. q [B, Hq, D], caches [NB, Hkv, BS, D], block_tables [B, max_blocks] int32,
     seq_lens [B] int32. partition_tokens: 0 direct, > 0 split, -1 library choice. ``max_seq_len`` is a
-    host hint (>= every seq_len); when omitted it is read from seq_lens (a device sync)."""
+    host hint (>= every seq_len); when omitted it is read from seq_lens (a device sync).
+    bf16 caches, or uint8 caches of fp8 (e4m3) codes with k_scale / v_scale (pkv_paged_attn_decode_fp8)."""
     lib = load_library()
     dev = q.device
     _need(q, "q", torch.bfloat16, 3, dev)
-    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
-    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    fp8 = k_cache.dtype == torch.uint8
+    cdt = torch.uint8 if fp8 else torch.bfloat16
+    _need(k_cache, "k_cache", cdt, 4, dev)
+    _need(v_cache, "v_cache", cdt, 4, dev)
+    if fp8 and (k_scale is None or v_scale is None):
+        raise ValueError("an fp8 cache needs k_scale and v_scale")
     _need(block_tables, "block_tables", torch.int32, 2, dev)
     _need(seq_lens, "seq_lens", torch.int32, 1, dev)
     B, Hq, D = q.shape
@@ -167,12 +179,41 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if fp8:
+        _check(lib.pkv_paged_attn_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                             _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, D, BS, NB,
+                                             block_tables.shape[1], int(max_seq_len), float(scale),
+                                             float(k_scale), float(v_scale), int(partition_tokens),
+                                             _ptr(workspace), wbytes, _stream(q)), "paged_attn_decode_fp8")
+        return out
     _check(lib.pkv_paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                      _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, D, BS, NB,
                                      block_tables.shape[1], int(max_seq_len), float(scale),
                                      int(partition_tokens), _ptr(workspace), wbytes, _stream(q)),
            "paged_attn_decode")
     return out
+
+
+def reshape_and_cache_fp8(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          slot_mapping: torch.Tensor, k_scale: float, v_scale: float) -> None:
+    """Scatter k/v [T, Hkv, D] (bf16) into fp8 caches [NB, Hkv, BS, D] (uint8 e4m3 codes) at
+    slot_mapping [T] (int64), storing the codes of k / k_scale and v / v_scale."""
+    lib = load_library()
+    dev = k.device
+    _need(k, "k", torch.bfloat16, 3, dev)
+    _need(v, "v", torch.bfloat16, 3, dev)
+    _need(k_cache, "k_cache", torch.uint8, 4, dev)
+    _need(v_cache, "v_cache", torch.uint8, 4, dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    T, Hkv, D = k.shape
+    NB, Hkv2, BS, D2 = k_cache.shape
+    if v.shape != k.shape or v_cache.shape != k_cache.shape or Hkv2 != Hkv or D2 != D:
+        raise ValueError("k/v/cache shapes disagree")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must have one entry per token")
+    _check(lib.pkv_reshape_and_cache_fp8(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+                                         T, Hkv, D, BS, NB, float(k_scale), float(v_scale), _stream(k)),
+           "reshape_and_cache_fp8")
 
 
 def ragged_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qo_indptr: torch.Tensor,

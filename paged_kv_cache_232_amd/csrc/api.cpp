@@ -71,12 +71,15 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
   return pkv::decode_workspace_layout(batch, num_q_heads, head_dim, max_seq_len, pt).total;
 }
 
-int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                          const int32_t* block_tables, const int32_t* seq_lens, void* out, float* lse,
-                          int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                          int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                          int32_t max_seq_len, float scale, int32_t partition_tokens, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* seq_lens, void* out, float* lse,
+                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                       int32_t max_seq_len, float scale, int32_t partition_tokens, void* workspace,
+                       size_t workspace_bytes, int kv_fp8, float k_scale, float v_scale,
+                       void* stream) {
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_seq_len < 0 || partition_tokens < -1)
     return PKV_E_INVALID_ARGUMENT;
@@ -109,6 +112,9 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_seq_len = max_seq_len;
   a.scale = scale;
+  a.kv_fp8 = kv_fp8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.partition_tokens =
       resolve_partition(batch, num_q_heads, num_kv_heads, max_seq_len, partition_tokens);
   if (a.partition_tokens > 0) {
@@ -124,6 +130,53 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
     a.max_partitions = wl.max_partitions;
   }
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+static bool scale_ok(float s) { return s > 0.f && s <= 3.4028235e38f; }
+
+extern "C" {
+
+int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, void* out, float* lse,
+                          int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t max_seq_len, float scale, int32_t partition_tokens, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                     max_seq_len, scale, partition_tokens, workspace, workspace_bytes, 0, 1.f, 1.f,
+                     stream);
+}
+
+int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                              float* lse, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                              float k_scale, float v_scale, int32_t partition_tokens,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_E_INVALID_ARGUMENT;
+  return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                     max_seq_len, scale, partition_tokens, workspace, workspace_bytes, 1, k_scale,
+                     v_scale, stream);
+}
+
+int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks, float k_scale,
+                              float v_scale, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return PKV_E_INVALID_ARGUMENT;
+  if (head_dim <= 0 || head_dim % 16 != 0 || block_size <= 0) return PKV_E_INVALID_ARGUMENT;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_E_INVALID_ARGUMENT;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_E_INVALID_ARGUMENT;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_E_INVALID_ARGUMENT;
+  return hip_status(pkv::launch_reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping,
+                                                      num_tokens, num_kv_heads, head_dim,
+                                                      block_size, num_blocks, k_scale, v_scale,
+                                                      (hipStream_t)stream));
 }
 
 static int check_prefill_common(const void* q, const void* out, const int32_t* qo_indptr,

@@ -111,6 +111,22 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+__device__ __forceinline__ u32x2 load8(const void* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// 8 fp8 (OCP e4m3) codes -> 8 bf16 (v_cvt_scalef32_pk_bf16_fp8 with scale 1: every e4m3 value,
+// subnormals and NaN included, is exactly representable in bf16). Element order is kept: byte j of
+// the input becomes bf16 j of the result.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 x) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true));
+  return r;
+}
+
 // Keeps the compiler from moving memory operations across this point. Loads that a loop keeps in
 // flight across iterations must be issued in the same order before the loop as inside it, or the
 // wait-count pass cannot tell their order at the loop head and waits for all of them.

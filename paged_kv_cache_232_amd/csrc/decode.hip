@@ -24,6 +24,8 @@
 //   * slots past the sequence length are masked by selection (their bits may be NaN).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -44,25 +46,38 @@ struct DecodeCfg {
   static_assert(WAVE_LDS >= D * 16 * 4, "combine buffer must fit in a wave's V tile");
 };
 
-template <int D>
+// One 32-token chunk in registers: per half page, each lane's K operand pieces and V pieces, 8
+// elements each (16 bytes of bf16, or 8 bytes of fp8 codes).
+template <int D, bool FP8>
 struct DecodeChunk {
-  u32x4 k[2][DecodeCfg<D>::KK];
-  u32x4 v[2][DecodeCfg<D>::VU];
+  using Piece = std::conditional_t<FP8, u32x2, u32x4>;
+  Piece k[2][DecodeCfg<D>::KK];
+  Piece v[2][DecodeCfg<D>::VU];
 };
+
+// 8 elements of a chunk piece as bf16 (fp8 e4m3 codes convert exactly)
+__device__ __forceinline__ u32x4 piece_bf16(u32x4 x) { return x; }
+__device__ __forceinline__ u32x4 piece_bf16(u32x2 x) { return fp8x8_to_bf16x8(x); }
+__device__ __forceinline__ u32x4 load_piece(const uint16_t* p, u32x4*) { return load16(p); }
+__device__ __forceinline__ u32x2 load_piece(const uint8_t* p, u32x2*) { return load8(p); }
 
 
 // scale_log2 > 0 always: the host folds a negative scale into negate_q (an exact sign flip of q)
 // and replaces a zero scale by the smallest normal float (every probability is then exactly 1).
-template <int D, int NW, bool SPLIT>
+template <int D, int NW, bool SPLIT, bool FP8>
 __global__ void __launch_bounds__(NW * kWave, D <= 128 ? 2 : 1)
-decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-              const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables,
+decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint8_t, uint16_t>* __restrict__ kc,
+              const std::conditional_t<FP8, uint8_t, uint16_t>* __restrict__ vc,
+              const int32_t* __restrict__ tables,
               const int32_t* __restrict__ lens, uint16_t* __restrict__ out,
               float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ m_part,
               float* __restrict__ l_part, int Hq, int Hkv, int G, int n_hg, int BS, int NB,
-              int max_blocks, int PT, int Pmax, float scale_log2, int negate_q, int bs_shift) {
+              int max_blocks, int PT, int Pmax, float scale_log2, float v_scale, int negate_q,
+              int bs_shift) {
   using C = DecodeCfg<D>;
-  using Chunk = DecodeChunk<D>;
+  using Chunk = DecodeChunk<D, FP8>;
+  using KVT = std::conditional_t<FP8, uint8_t, uint16_t>;
+  using Piece = typename Chunk::Piece;
   __shared__ __attribute__((aligned(16))) char smem[NW * C::WAVE_LDS];
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
@@ -135,12 +150,12 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
       const int blk = clampi(tw.get(tk >> bs_shift, lane), 0, NB - 1);
       const size_t base = (size_t)blk * block_stride + (size_t)kh * head_stride +
                           (size_t)(tk & (BS - 1)) * D;
-      const uint16_t* kp = kc + base;
-      const uint16_t* vp = vc + base;
+      const KVT* kp = kc + base;
+      const KVT* vp = vc + base;
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) ch.k[hh][kk] = load16(kp + koff + kk * 32);
+      for (int kk = 0; kk < C::KK; ++kk) ch.k[hh][kk] = load_piece(kp + koff + kk * 32, (Piece*)nullptr);
 #pragma unroll
-      for (int i = 0; i < C::VU; ++i) ch.v[hh][i] = load16(vp + voff + i * 512);
+      for (int i = 0; i < C::VU; ++i) ch.v[hh][i] = load_piece(vp + voff + i * 512, (Piece*)nullptr);
     }
   };
 
@@ -153,7 +168,8 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     for (int hh = 0; hh < 2; ++hh) {
       s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) s[hh] = mfma16(as_bf16x8(ch.k[hh][kk]), qreg[kk], s[hh]);
+      for (int kk = 0; kk < C::KK; ++kk)
+        s[hh] = mfma16(as_bf16x8(piece_bf16(ch.k[hh][kk])), qreg[kk], s[hh]);
     }
     // stage V rows in LDS; rows past the end are zeroed (select, so NaN slack never leaks)
     if (!partial) {
@@ -163,7 +179,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
         for (int i = 0; i < C::VU; ++i) {
           const int u = i * 64 + lane;
           const int row = u / (D / 8);
-          *reinterpret_cast<u32x4*>(vbuf + (16 * hh + row) * C::RS + (u - row * (D / 8)) * 16) = ch.v[hh][i];
+          *reinterpret_cast<u32x4*>(vbuf + (16 * hh + row) * C::RS + (u - row * (D / 8)) * 16) = piece_bf16(ch.v[hh][i]);
         }
     } else {
 #pragma unroll
@@ -172,7 +188,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
         for (int i = 0; i < C::VU; ++i) {
           const int u = i * 64 + lane;
           const int row = u / (D / 8);
-          u32x4 val = ch.v[hh][i];
+          u32x4 val = piece_bf16(ch.v[hh][i]);
           if (cs + 16 * hh + row > last) val = u32x4{0, 0, 0, 0};
           *reinterpret_cast<u32x4*>(vbuf + (16 * hh + row) * C::RS + (u - row * (D / 8)) * 16) = val;
         }
@@ -255,7 +271,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     // a single wave owns the whole work item: normalise and write straight from registers
     if (!col_ok) return;
     const int hout = kh * G + gcol;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float inv = l_run > 0.f ? v_scale / l_run : 0.f;
     if constexpr (SPLIT) {
       const size_t pi = ((size_t)b * Pmax + p) * Hq + hout;
       float* op = o_part + pi * D + 4 * qg;
@@ -305,7 +321,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
       f[w2] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
       lsum += f[w2] * sm_l[w2][oc];
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float inv = lsum > 0.f ? v_scale / lsum : 0.f;
     float acc[DPT];
 #pragma unroll
     for (int i = 0; i < DPT; ++i) {
@@ -440,22 +456,27 @@ DecodeWorkspaceLayout decode_workspace_layout(int batch, int num_q_heads, int he
   return w;
 }
 
-template <int D>
+template <int D, bool FP8>
 static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
+  using KVT = std::conditional_t<FP8, uint8_t, uint16_t>;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int n_hg = (G + 15) / 16;
-  float scale_log2 = a.scale * kLog2e;
+  // fp8 cache: scores are q . code * (scale * k_scale), outputs sum p * code * v_scale
+  const float k_scale = FP8 ? a.k_scale : 1.f;
+  const float v_scale = FP8 ? a.v_scale : 1.f;
+  float scale_log2 = a.scale * k_scale * kLog2e;
   const int negate_q = scale_log2 < 0.f;
   if (negate_q) scale_log2 = -scale_log2;
   if (!(scale_log2 >= 1.17549435e-38f)) scale_log2 = 1.17549435e-38f;  // zero (or denormal) scale
+  const int bs_shift = __builtin_ctz((unsigned)a.block_size);
   if (a.partition_tokens > 0) {
     const dim3 grid(a.max_partitions, a.num_kv_heads * n_hg, a.batch);
-    hipLaunchKernelGGL((decode_kernel<D, 1, true>), grid, dim3(kWave), 0, stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache,
+    hipLaunchKernelGGL((decode_kernel<D, 1, true, FP8>), grid, dim3(kWave), 0, stream,
+                       (const uint16_t*)a.q, (const KVT*)a.k_cache, (const KVT*)a.v_cache,
                        a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, a.o_part, a.m_part,
                        a.l_part, a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size,
                        a.num_blocks, a.max_blocks_per_seq, a.partition_tokens, a.max_partitions,
-                       scale_log2, negate_q, __builtin_ctz((unsigned)a.block_size));
+                       scale_log2, v_scale, negate_q, bs_shift);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // long splits take 1024 threads per (head, sequence), so one batch of loads covers them
@@ -471,22 +492,26 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const dim3 grid(1, a.num_kv_heads * n_hg, a.batch);
-  hipLaunchKernelGGL((decode_kernel<D, kDirectWaves, false>), grid, dim3(kDirectWaves * kWave), 0,
-                     stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
-                     (const uint16_t*)a.v_cache, a.block_tables, a.seq_lens, (uint16_t*)a.out,
-                     a.lse, nullptr, nullptr, nullptr, a.num_q_heads, a.num_kv_heads, G, n_hg,
-                     a.block_size, a.num_blocks, a.max_blocks_per_seq, 0, 1, scale_log2, negate_q,
-                     __builtin_ctz((unsigned)a.block_size));
+  hipLaunchKernelGGL((decode_kernel<D, kDirectWaves, false, FP8>), grid, dim3(kDirectWaves * kWave),
+                     0, stream, (const uint16_t*)a.q, (const KVT*)a.k_cache, (const KVT*)a.v_cache,
+                     a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, nullptr, nullptr, nullptr,
+                     a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size, a.num_blocks,
+                     a.max_blocks_per_seq, 0, 1, scale_log2, v_scale, negate_q, bs_shift);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+template <bool FP8>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   switch (a.head_dim) {
-    case 64: return launch_decode_d<64>(a, stream);
-    case 128: return launch_decode_d<128>(a, stream);
-    case 256: return launch_decode_d<256>(a, stream);
+    case 64: return launch_decode_d<64, FP8>(a, stream);
+    case 128: return launch_decode_d<128, FP8>(a, stream);
+    case 256: return launch_decode_d<256, FP8>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  return a.kv_fp8 ? launch_decode_t<true>(a, stream) : launch_decode_t<false>(a, stream);
 }
 
 }  // namespace pkv

@@ -25,6 +25,8 @@ struct DecodeArgs {
   int max_seq_len;
   float scale;
   int partition_tokens;  // 0 = direct, > 0 = split
+  int kv_fp8;            // caches hold fp8 (e4m3) codes dequantised by k_scale / v_scale
+  float k_scale, v_scale;
   // split workspace (null for direct)
   float* o_part;
   float* m_part;
@@ -62,6 +64,12 @@ struct PrefillArgs {
 };
 
 hipError_t launch_ragged_prefill(const PrefillArgs& a, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                                        const int64_t* slot_mapping, int num_tokens,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, float k_scale, float v_scale,
+                                        hipStream_t stream);
 
 hipError_t launch_copy_blocks(const uint64_t* k_ptrs, const uint64_t* v_ptrs, int num_layers,
                               const int64_t* mapping, int num_pairs, int64_t block_bytes,

@@ -1,0 +1,131 @@
+"""GPU fp8 (e4m3) KV cache against the oracle, through the C ABI: the quantising scatter bit-exact,
+decode over an fp8 cache (quantised by the oracle) within the parity gate."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_232_amd as pkv
+from parity import assert_parity
+from workloads import make_config, paged_decode_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _codes(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).view(torch.uint8)
+
+
+@pytest.mark.parametrize("hkv,d,bs,scales", [(4, 256, 16, (0.05, 0.02)), (8, 128, 16, (1.0, 1.0)),
+                                              (2, 64, 32, (3.7, 0.6))])
+def test_fp8_scatter_bit_exact(hkv, d, bs, scales):
+    g = torch.Generator().manual_seed(d + hkv)
+    T, nb = 300, 40
+    k = (torch.randn(T, hkv, d, generator=g) * 8).to(torch.bfloat16)
+    v = (torch.randn(T, hkv, d, generator=g) * 8).to(torch.bfloat16)
+    # special inputs: saturation, infinities, NaN, zeros of both signs, tiny values (subnormal codes)
+    k[0, 0, :6] = torch.tensor([1e5, -1e5, float("inf"), float("-inf"), float("nan"), -0.0])
+    v[1, 0, :4] = torch.tensor([3e-5, -7e-6, 0.0, 1e-30])
+    slots = torch.randperm(nb * bs, generator=g)[:T].to(torch.int64)
+    slots[5] = -1
+    kc0 = torch.randint(0, 256, (nb, hkv, bs, d), generator=g, dtype=torch.int32).to(torch.uint8)
+    vc0 = torch.randint(0, 256, (nb, hkv, bs, d), generator=g, dtype=torch.int32).to(torch.uint8)
+    ek, ev = oracle.reshape_and_cache_fp8(k, v, kc0, vc0, slots, *scales)
+    kc, vc = kc0.to(DEV), vc0.to(DEV)
+    pkv.reshape_and_cache_fp8(k.to(DEV), v.to(DEV), kc, vc, slots.to(DEV), *scales)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), ek), "k codes differ from the oracle"
+    assert np.array_equal(vc.cpu().numpy(), ev), "v codes differ from the oracle"
+
+
+def _fp8_inputs(di, k_scale, v_scale):
+    return oracle.quantize(di.k_cache, k_scale), oracle.quantize(di.v_cache, v_scale)
+
+
+def _decode_fp8(di, kq, vq, k_scale, v_scale, pt, with_lse=False):
+    q = di.q.to(DEV)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=DEV) if with_lse else None
+    out = pkv.paged_attn_decode(q, _codes(kq).to(DEV), _codes(vq).to(DEV), di.block_tables.to(DEV),
+                                di.seq_lens.to(DEV), di.scale, max_seq_len=di.max_seq_len,
+                                partition_tokens=pt, lse=lse, k_scale=k_scale, v_scale=v_scale)
+    torch.cuda.synchronize()
+    return out.cpu(), (lse.cpu() if with_lse else None)
+
+
+@pytest.mark.parametrize("pt", [0, 32, 512, -1])
+def test_fp8_tiny_decode(pt):
+    di = make_config(1)
+    kq, vq = _fp8_inputs(di, 0.25, 0.5)
+    ref, rlse = oracle.paged_decode_fp8(di.q, kq, vq, di.block_tables, di.seq_lens, di.scale, 0.25, 0.5,
+                                        return_lse=True)
+    out, lse = _decode_fp8(di, kq, vq, 0.25, 0.5, pt, with_lse=True)
+    print(f"fp8 tiny decode pt={pt}", assert_parity(out, ref, f"fp8 tiny decode pt={pt}"))
+    np.testing.assert_allclose(lse.double().numpy(), rlse, rtol=0, atol=2e-3)
+
+
+FP8_SHAPES = [
+    # lens, Hq, Hkv, D, BS
+    ([15, 16, 17, 0], 4, 2, 128, 16),
+    ([1000, 1, 513, 512], 8, 2, 128, 16),
+    ([300, 129], 32, 1, 64, 16),
+    ([700, 3], 16, 2, 256, 16),
+    ([333, 77], 8, 4, 128, 32),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FP8_SHAPES)))
+@pytest.mark.parametrize("pt", [0, 512])
+def test_fp8_decode_shapes(case, pt):
+    lens, hq, hkv, d, bs = FP8_SHAPES[case]
+    di = paged_decode_inputs(3000 + case, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seq_lens=lens,
+                             block_size=bs)
+    kq, vq = _fp8_inputs(di, 0.125, 0.0625)
+    ref = oracle.paged_decode_fp8(di.q, kq, vq, di.block_tables, di.seq_lens, di.scale, 0.125, 0.0625)
+    out, _ = _decode_fp8(di, kq, vq, 0.125, 0.0625, pt)
+    print(f"fp8 decode case {case} pt={pt}", assert_parity(out, ref, f"fp8 decode case {case} pt {pt}"))
+
+
+def test_fp8_batched_decode_both_paths():
+    # the batched-decode shape (32 q / 8 kv heads, hd 128, block 16) at 8 sequences
+    di = paged_decode_inputs(3100, num_q_heads=32, num_kv_heads=8, head_dim=128, len_range=(256, 1536),
+                             batch=8)
+    kq, vq = _fp8_inputs(di, 0.02, 0.02)
+    ref = oracle.paged_decode_fp8(di.q, kq, vq, di.block_tables, di.seq_lens, di.scale, 0.02, 0.02)
+    for pt in (0, 512):
+        out, _ = _decode_fp8(di, kq, vq, 0.02, 0.02, pt)
+        print(f"fp8 batched decode pt={pt}", assert_parity(out, ref, f"fp8 batched decode pt={pt}"))
+
+
+def test_fp8_long_context_split_decode():
+    # the long-context shape (64 q / 8 kv heads, hd 128, partitions of 512) at 8192 tokens
+    di = paged_decode_inputs(3200, num_q_heads=64, num_kv_heads=8, head_dim=128, seq_lens=[8192])
+    kq, vq = _fp8_inputs(di, 0.05, 0.05)
+    ref = oracle.paged_decode_fp8(di.q, kq, vq, di.block_tables, di.seq_lens, di.scale, 0.05, 0.05)
+    out, _ = _decode_fp8(di, kq, vq, 0.05, 0.05, 512)
+    print("fp8 long split decode", assert_parity(out, ref, "fp8 long split decode"))
+
+
+def test_fp8_gpu_scatter_then_decode_equals_oracle():
+    # new tokens quantised by the GPU scatter, then decoded: the caches equal the oracle's (the
+    # scatter is bit-exact), so the decode matches the oracle over the oracle's own caches
+    di = paged_decode_inputs(3300, num_q_heads=8, num_kv_heads=2, head_dim=128, seq_lens=[200, 77])
+    k_scale, v_scale = 0.1, 0.2
+    kq, vq = _fp8_inputs(di, k_scale, v_scale)
+    g = torch.Generator().manual_seed(1)
+    newk = torch.randn(2, 2, 128, generator=g).to(torch.bfloat16)
+    newv = torch.randn(2, 2, 128, generator=g).to(torch.bfloat16)
+    bs = di.block_size
+    tables = di.block_tables
+    slots = torch.tensor([int(tables[0, 200 // bs]) * bs + 200 % bs, int(tables[1, 77 // bs]) * bs + 77 % bs])
+    ek, ev = oracle.reshape_and_cache_fp8(newk, newv, kq, vq, slots, k_scale, v_scale)
+    kc, vc = _codes(kq).to(DEV), _codes(vq).to(DEV)
+    pkv.reshape_and_cache_fp8(newk.to(DEV), newv.to(DEV), kc, vc, slots.to(DEV), k_scale, v_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), ek) and np.array_equal(vc.cpu().numpy(), ev)
+    lens = torch.tensor([201, 78], dtype=torch.int32)
+    ref = oracle.paged_decode_fp8(di.q, ek, ev, tables, lens, di.scale, k_scale, v_scale)
+    out = pkv.paged_attn_decode(di.q.to(DEV), kc, vc, tables.to(DEV), lens.to(DEV), di.scale, max_seq_len=201,
+                                partition_tokens=0, k_scale=k_scale, v_scale=v_scale)
+    torch.cuda.synchronize()
+    print("fp8 scatter+decode", assert_parity(out.cpu(), ref, "fp8 scatter then decode"))
