@@ -10,8 +10,9 @@ One step runs every call of the hot path once, on inputs already resident in HBM
 Each call is bracketed by HIP events on the stream it is launched on. The headline value is the
 decode KV bandwidth (algorithmic bytes of calls 3 and 4 over their measured time); the ragged
 prefill TFLOP/s is reported beside it. The direct and split decode paths of workload 3, decode of
-workloads 3 and 4 over an fp8 (e4m3) cache, and the block-management calls (copy_blocks over 32
-layers, swap_blocks to pinned host memory) are timed separately, outside the step.
+workloads 3 and 4 over an fp8 (e4m3) cache, a small decode step (eager and replayed from a HIP
+graph), and the block-management calls (copy_blocks over 32 layers, swap_blocks to pinned host
+memory) are timed separately, outside the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --calibrate-copy     (times a plain 1 GiB device copy, for counter scaling)
@@ -208,6 +209,40 @@ def build_cases(dev):
         meta[f"lens{cid}_sum"] = sum(lens)
         meta[f"flops{cid}"] = decode_flops(lens, Hq, D)
         del di
+    # a small decode step (scatter of each sequence's new token, then decode), eager and replayed
+    # from a HIP graph captured once with the planner's real maximum length
+    from workloads import paged_decode_inputs
+    cap = [int(x) for x in torch.randint(512, 2049, (8,), generator=torch.Generator().manual_seed(232200))]
+    sd = paged_decode_inputs(232201, num_q_heads=32, num_kv_heads=8, head_dim=128, seq_lens=cap)
+    ds = dict(q=sd.q.to(dev), kc=sd.k_cache.to(dev), vc=sd.v_cache.to(dev), bt=sd.block_tables.to(dev),
+              sl=sd.seq_lens.to(dev), kn=torch.randn(8, 8, 128, device=dev).to(torch.bfloat16))
+    ds["vn"] = ds["kn"].clone()
+    pos = [L - 1 for L in cap]
+    ds["slots"] = torch.tensor([int(sd.block_tables[b, p // 16]) * 16 + p % 16 for b, p in enumerate(pos)],
+                               dtype=torch.int64, device=dev)
+    mx, ptp, wsb = pkv.decode_plan(cap, 32, 8, 128)
+    ds["ws"] = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    ds["out"] = torch.empty_like(ds["q"])
+
+    def small_step(ds=ds, mx=mx, ptp=ptp):
+        pkv.reshape_and_cache(ds["kn"], ds["vn"], ds["kc"], ds["vc"], ds["slots"])
+        pkv.paged_attn_decode(ds["q"], ds["kc"], ds["vc"], ds["bt"], ds["sl"], sd.scale, max_seq_len=mx,
+                              partition_tokens=ptp, out=ds["out"], workspace=ds["ws"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        small_step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        small_step()
+    sbytes = decode_bytes(cap, 32, 8, 128, 16) + scatter_bytes(8, 8, 128)
+    cases["decode_step_eager"] = Case("decode step, eager launches (scatter + decode, B=8, U[512,2048])",
+                                      small_step, "hbm", sbytes, "GB/s")
+    cases["decode_step_graph"] = Case("decode step replayed from a HIP graph (same step)", graph.replay, "hbm",
+                                      sbytes, "GB/s")
+    meta["graph"] = graph  # keep the captured graph alive
+
     # block management around the cache (timed alone, outside the step): copy_blocks over 32
     # layers of the batched-decode cache shape, and a swap-out of 256 blocks to pinned host memory
     g = torch.Generator().manual_seed(232100)
@@ -231,7 +266,8 @@ def build_cases(dev):
 
 STEP = ["scatter5", "paged5", "ragged2", "decode3", "decode4"]
 # timed alone, outside the step
-EXTRA = ["decode3_direct", "decode3_split", "decode3_fp8", "decode4_fp8", "copy_blocks", "swap_out"]
+EXTRA = ["decode3_direct", "decode3_split", "decode3_fp8", "decode4_fp8", "decode_step_eager", "decode_step_graph",
+         "copy_blocks", "swap_out"]
 
 
 def time_step(cases, steps, warmup):
@@ -285,17 +321,17 @@ def cpu_baseline(meta):
     import oracle
     di = make_config(3)
     spec = CONFIGS[3]
-    n = 8  # first 8 of the 64 sequences
+    n = 32  # first 32 of the 64 sequences (about 10 s of the oracle on 8 to 16 host cores)
     lens = di.seq_lens[:n].tolist()
     t0 = time.perf_counter()
     oracle.paged_decode(di.q[:n], di.k_cache, di.v_cache, di.block_tables[:n], di.seq_lens[:n], di.scale)
     dt = time.perf_counter() - t0
     work = decode_bytes(lens, spec["num_q_heads"], spec["num_kv_heads"], spec["head_dim"], di.block_size)
     gbs = work / dt / 1e9
-    # prefill sample: the shortest request of the ragged workload
+    # prefill sample: the longest request of the ragged workload
     ri = make_config(2)
     lens2 = meta["lens2"]
-    b = int(np.argmin(lens2))
+    b = int(np.argmax(lens2))
     q0, q1 = int(ri.qo_indptr[b]), int(ri.qo_indptr[b + 1])
     import torch as _t
     qi = _t.tensor([0, q1 - q0], dtype=_t.int32)

@@ -71,6 +71,24 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
                                   int32_t head_dim, int32_t max_seq_len, int32_t partition_tokens);
 
 /*
+ * Decode plan from the host copy of the sequence lengths, for callers that size a launch once and
+ * capture it in a HIP graph. The libmir-cuda page plans direct vs split decode ahead of capture
+ * (PagedAttentionBf16::new, plan_attention, captured_configs); the vLLM-derived paged_attn.py page
+ * (forward_decode) routes on the real seq_lens.max(), not on a bound inflated for graph mode.
+ *   seq_lens_h           HOST int32 [batch] (>= 0).
+ *   partition_tokens     as for pkv_paged_attn_decode (0, > 0 multiple of 32, or -1).
+ *   *max_seq_len_out     the real maximum length (pass it as max_seq_len);
+ *   *partition_tokens_out the path pkv_paged_attn_decode takes for it (0 = direct);
+ *   *workspace_bytes_out the workspace that call needs.
+ * A captured call reads seq_lens from device memory on every replay, so it serves any lengths up to
+ * the max_seq_len it was captured with; plan (and capture) again when that bound changes.
+ */
+int pkv_decode_plan(const int32_t* seq_lens_h, int32_t batch, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t partition_tokens,
+                    int32_t* max_seq_len_out, int32_t* partition_tokens_out,
+                    size_t* workspace_bytes_out);
+
+/*
  * paged_attn_decode — one query token per sequence against its paged KV cache.
  * Defined by the vLLM-derived paged_attn.py page (PagedAttention._forward_decode_pytorch and
  * forward_decode): out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over tokens [0, seq_lens[b]),

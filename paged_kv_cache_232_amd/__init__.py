@@ -50,6 +50,8 @@ _SIGNATURES = {
                                                  _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                                  _c_i32, _c_f32, _c_f32, _c_f32, _c_i32, _c_ptr, _c_size,
                                                  _c_ptr]),
+    "pkv_decode_plan": (ctypes.c_int, [_c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
+                                       _c_ptr]),
     "pkv_copy_blocks": (ctypes.c_int, [_c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i64, _c_i32, _c_ptr]),
     "pkv_swap_blocks": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i64, _c_i32, _c_i32, _c_ptr]),
 }
@@ -214,6 +216,19 @@ def reshape_and_cache_fp8(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tenso
     _check(lib.pkv_reshape_and_cache_fp8(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
                                          T, Hkv, D, BS, NB, float(k_scale), float(v_scale), _stream(k)),
            "reshape_and_cache_fp8")
+
+
+def decode_plan(seq_lens_h, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                partition_tokens: int = -1):
+    """(max_seq_len, partition_tokens, workspace_bytes) that paged_attn_decode uses for these host
+    lengths: size a workspace and a max_seq_len once, e.g. before capturing the call in a graph."""
+    lens = _host_i32(seq_lens_h)
+    mx, pt, ws = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
+    _check(load_library().pkv_decode_plan(ctypes.c_void_p(lens.data_ptr()) if lens.numel() else None,
+                                          lens.numel(), num_q_heads, num_kv_heads, head_dim,
+                                          int(partition_tokens), ctypes.byref(mx), ctypes.byref(pt),
+                                          ctypes.byref(ws)), "decode_plan")
+    return mx.value, pt.value, ws.value
 
 
 def ragged_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qo_indptr: torch.Tensor,

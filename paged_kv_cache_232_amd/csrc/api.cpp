@@ -62,6 +62,29 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
                                                   (hipStream_t)stream));
 }
 
+int pkv_decode_plan(const int32_t* seq_lens_h, int32_t batch, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t partition_tokens,
+                    int32_t* max_seq_len_out, int32_t* partition_tokens_out,
+                    size_t* workspace_bytes_out) {
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || partition_tokens < -1)
+    return PKV_E_INVALID_ARGUMENT;
+  if (num_q_heads % num_kv_heads != 0) return PKV_E_INVALID_ARGUMENT;
+  if (!head_dim_ok(head_dim)) return PKV_E_UNSUPPORTED;
+  if (partition_tokens > 0 && partition_tokens % 32 != 0) return PKV_E_UNSUPPORTED;
+  if (!max_seq_len_out || !partition_tokens_out || !workspace_bytes_out) return PKV_E_INVALID_ARGUMENT;
+  if (batch > 0 && !seq_lens_h) return PKV_E_INVALID_ARGUMENT;
+  int32_t mx = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens_h[b] < 0) return PKV_E_INVALID_ARGUMENT;
+    if (seq_lens_h[b] > mx) mx = seq_lens_h[b];
+  }
+  const int pt = batch > 0 ? resolve_partition(batch, num_q_heads, num_kv_heads, mx, partition_tokens) : 0;
+  *max_seq_len_out = mx;
+  *partition_tokens_out = pt;
+  *workspace_bytes_out = batch > 0 ? pkv::decode_workspace_layout(batch, num_q_heads, head_dim, mx, pt).total : 0;
+  return PKV_OK;
+}
+
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_seq_len, int32_t partition_tokens) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0)

@@ -24,7 +24,7 @@ def _declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = pkv.load_library()
     syms = _declared_symbols()
-    assert len(syms) == 11, syms
+    assert len(syms) == 12, syms
     for s in syms:
         assert hasattr(lib, s), f"{s} missing from libpkv.so"
     assert set(syms) == set(pkv._SIGNATURES), "binding and header disagree"
@@ -126,3 +126,20 @@ def test_block_calls_argument_errors():
     assert lib.pkv_swap_blocks(fake, fake, mp, 2, 64, 4, 4, nul) == pkv.E_INVALID_ARGUMENT
     assert lib.pkv_swap_blocks(fake, fake, mp, 2, 0, 8, 8, nul) == pkv.E_INVALID_ARGUMENT
     assert lib.pkv_swap_blocks(nul, nul, nul, 0, 64, 4, 4, nul) == pkv.OK
+
+
+def test_decode_plan_uses_the_real_maximum():
+    lens = [100, 7000, 3000, 0]
+    # few work-groups and long sequences: split 512; the workspace is what the decode call asks for
+    mx, pt, ws = pkv.decode_plan(lens, 32, 8, 128)
+    assert mx == 7000 and pt == 512
+    assert ws == pkv.decode_workspace_bytes(4, 32, 8, 128, 7000, 512)
+    # an explicit path is kept; direct needs no workspace
+    assert pkv.decode_plan(lens, 32, 8, 128, 0) == (7000, 0, 0)
+    # enough (sequence, kv head) groups: direct
+    assert pkv.decode_plan([4096] * 64, 32, 8, 128)[1] == 0
+    # short sequences stay direct whatever the batch
+    assert pkv.decode_plan([300, 512], 32, 8, 128)[1] == 0
+    assert pkv.decode_plan([], 32, 8, 128) == (0, 0, 0)
+    with pytest.raises(pkv.PkvError):
+        pkv.decode_plan([5, -1], 32, 8, 128)
