@@ -29,3 +29,4 @@ from .blocks import copy_blocks, swap_blocks  # noqa: F401,E402
 from .fp8 import (  # noqa: F401,E402
     e4m3_value, e4m3_decode, e4m3_encode, quantize, dequantize, reshape_and_cache_fp8, paged_decode_fp8,
 )
+from .stream import paged_decode_window, streamed_decode  # noqa: F401,E402

@@ -624,3 +624,81 @@ def test_fp8_scatter_matches_quantized_bf16_scatter():
     for s in range(nb * bs):
         if s not in written:
             assert not kc[s // bs, :, s % bs].any()
+
+
+# ----------------------------------------------------------------------------------------------
+# Sliding window and streamed (multi-launch) decode attention
+# ----------------------------------------------------------------------------------------------
+def _small_decode(seed=21, lens=(50, 17, 33, 0), hq=4, hkv=2, d=16):
+    import torch
+    g = torch.Generator().manual_seed(seed)
+    bs, nb = 8, 24
+    q = torch.randn(len(lens), hq, d, generator=g, dtype=torch.float64)
+    kc = torch.randn(nb, hkv, bs, d, generator=g, dtype=torch.float64)
+    vc = torch.randn(nb, hkv, bs, d, generator=g, dtype=torch.float64)
+    perm = torch.randperm(nb, generator=g)
+    tables = torch.full((len(lens), 8), -1, dtype=torch.int64)
+    k = 0
+    for b, L in enumerate(lens):
+        n = -(-L // bs)
+        tables[b, :n] = perm[k:k + n]
+        k += n
+    return q, kc, vc, tables, torch.tensor(lens), bs
+
+
+def test_window_matches_sdpa_with_a_window_mask():
+    import torch
+    q, kc, vc, tables, lens, bs = _small_decode()
+    W = 13
+    got = oracle.paged_decode_window(q, kc, vc, tables, lens, 0.3, W)
+    for b, L in enumerate(lens.tolist()):
+        if L == 0:
+            assert not got[b].any()
+            continue
+        t = torch.arange(L)
+        blk, off = tables[b, t // bs], t % bs
+        for h in range(q.shape[1]):
+            kh = h // 2
+            K, V = kc[blk, kh, off], vc[blk, kh, off]
+            mask = t >= L - W
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[b, h][None, None, None], K[None, None], V[None, None], attn_mask=mask[None, None, None],
+                scale=0.3)[0, 0, 0]
+            np.testing.assert_allclose(got[b, h], ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_window_special_cases():
+    q, kc, vc, tables, lens, bs = _small_decode()
+    full = oracle.paged_decode(q, kc, vc, tables, lens, 0.3)
+    np.testing.assert_array_equal(oracle.paged_decode_window(q, kc, vc, tables, lens, 0.3, 0), full)
+    np.testing.assert_array_equal(oracle.paged_decode_window(q, kc, vc, tables, lens, 0.3, 1000), full)
+    # a window of one token returns that token's value row exactly
+    one = oracle.paged_decode_window(q, kc, vc, tables, lens, 0.3, 1)
+    for b, L in enumerate(lens.tolist()):
+        if L:
+            t = L - 1
+            np.testing.assert_array_equal(one[b, 0], vc[tables[b, t // bs], 0, t % bs].numpy())
+
+
+def test_streamed_tiles_equal_one_pass_in_any_order():
+    import torch
+    q, kc, vc, tables, lens, bs = _small_decode(lens=(50, 17, 33, 40))
+    full, flse = oracle.paged_decode(q, kc, vc, tables, lens, 0.3, return_lse=True)
+    # split every table row into tiles of at most 3 blocks; the last block of a sequence's final
+    # tile holds only its valid slots
+    cap = 3
+    tiles = []
+    for i in range(0, 8, cap):
+        t_tab = torch.full((4, cap), -1, dtype=torch.int64)
+        t_len = torch.zeros(4, dtype=torch.int64)
+        for b, L in enumerate(lens.tolist()):
+            nblk = -(-L // bs)
+            blocks = tables[b, i:min(i + cap, nblk)]
+            t_tab[b, :len(blocks)] = blocks
+            t_len[b] = max(0, min(L - i * bs, cap * bs))
+        tiles.append((t_tab, t_len))
+    got, glse = oracle.streamed_decode(q, kc, vc, tiles, 0.3, return_lse=True)
+    np.testing.assert_allclose(got, full, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(glse, flse, rtol=0, atol=1e-12)
+    got_rev = oracle.streamed_decode(q, kc, vc, tiles[::-1], 0.3)
+    np.testing.assert_allclose(got_rev, full, rtol=0, atol=1e-12)
