@@ -163,6 +163,51 @@ int pkv_validate_block_tables_h(const int32_t* block_tables_h, const int32_t* se
                                 int32_t num_blocks);
 
 /*
+ * paged_attn_decode with a sliding window: as pkv_paged_attn_decode (same arguments, paths and
+ * workspace), with sequence b attending only to its keys [max(0, seq_lens[b] - window), seq_lens[b]).
+ * window == 0 means no window; window < 0 is PKV_E_INVALID_ARGUMENT. The vLLM-derived paged_attn.py
+ * page's forward_decode takes a sliding_window, and the libmir-cuda page sizes its split partitions
+ * by (token_count, window) (captured_configs).
+ */
+int pkv_paged_attn_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                                 float* lse, int32_t batch, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, int32_t max_blocks_per_seq,
+                                 int32_t max_seq_len, float scale, int32_t window,
+                                 int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * Streamed decode attention over several launches, one per tile of resident blocks, as the Atlas
+ * spark_storage/high_speed_swap/impl_more.rs page runs it (attend_layer_on_stream_with_q_pos: a step
+ * begins, each tile of at most resident_blocks blocks is attended through its own block table, the
+ * output is normalised at the end). The result equals one decode over the union of the tiles' tokens.
+ *
+ *   state  caller-owned device buffer of pkv_stream_attn_state_bytes(batch, num_q_heads, head_dim)
+ *          bytes holding, per (sequence, q head), the normalised fp32 output row, the running max
+ *          (log2 units) and the exp-sum: [B, Hq, D] f32, then [B, Hq] f32 twice, each 256-byte
+ *          aligned. Opaque to the caller otherwise.
+ *   begin     resets the state (a fill kernel: safe inside a captured graph).
+ *   step      attends q to one tile: tile_tables [batch, tile_capacity] int32 (physical blocks, in
+ *             token order within the tile), tile_lens [batch] int32 (tokens of the tile: a sequence's
+ *             last block may be partly valid, slots past tile_lens are never read; 0 = nothing), and
+ *             folds the tile into the state. Tiles may come in any order.
+ *   finalize  out [batch, num_q_heads, head_dim] bf16 = the normalised output (zero rows for
+ *             sequences no tile touched); lse optional [batch, num_q_heads] f32 (natural log).
+ */
+size_t pkv_stream_attn_state_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim);
+int pkv_stream_attn_begin(void* state, size_t state_bytes, int32_t batch, int32_t num_q_heads,
+                          int32_t head_dim, void* stream);
+int pkv_stream_attn_step(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* tile_tables, const int32_t* tile_lens, void* state,
+                         size_t state_bytes, int32_t batch, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, int32_t tile_capacity, float scale, void* stream);
+int pkv_stream_attn_finalize(const void* state, size_t state_bytes, void* out, float* lse,
+                             int32_t batch, int32_t num_q_heads, int32_t head_dim, void* stream);
+
+/*
  * FP8 KV cache. The vLLM-derived paged_attn.py page passes kv_cache_dtype with per-tensor k_scale
  * and v_scale floats to write_to_paged_cache and forward_decode. Here the fp8 cache holds OCP FP8
  * E4M3 codes (bias 7, no infinities, max 448, S.1111.111 = NaN) in the same

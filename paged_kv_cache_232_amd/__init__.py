@@ -52,6 +52,15 @@ _SIGNATURES = {
                                                  _c_ptr]),
     "pkv_decode_plan": (ctypes.c_int, [_c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr,
                                        _c_ptr]),
+    "pkv_paged_attn_decode_window": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                                    _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                    _c_i32, _c_f32, _c_i32, _c_i32, _c_ptr, _c_size, _c_ptr]),
+    "pkv_stream_attn_state_bytes": (_c_size, [_c_i32, _c_i32, _c_i32]),
+    "pkv_stream_attn_begin": (ctypes.c_int, [_c_ptr, _c_size, _c_i32, _c_i32, _c_i32, _c_ptr]),
+    "pkv_stream_attn_step": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_i32,
+                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_ptr]),
+    "pkv_stream_attn_finalize": (ctypes.c_int, [_c_ptr, _c_size, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
+                                                _c_ptr]),
     "pkv_copy_blocks": (ctypes.c_int, [_c_ptr, _c_ptr, _c_i32, _c_ptr, _c_i32, _c_i64, _c_i32, _c_ptr]),
     "pkv_swap_blocks": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i64, _c_i32, _c_i32, _c_ptr]),
 }
@@ -149,7 +158,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       max_seq_len: Optional[int] = None, partition_tokens: int = -1,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, k_scale: Optional[float] = None,
-                      v_scale: Optional[float] = None) -> torch.Tensor:
+                      v_scale: Optional[float] = None, window: int = 0) -> torch.Tensor:
     """Decode attention. q [B, Hq, D], caches [NB, Hkv, BS, D], block_tables [B, max_blocks] int32,
     seq_lens [B] int32. partition_tokens: 0 direct, > 0 split, -1 library choice. ``max_seq_len`` is a
     host hint (>= every seq_len); when omitted it is read from seq_lens (a device sync).
@@ -181,6 +190,15 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if window:
+        if fp8:
+            raise ValueError("a sliding window is supported on bf16 caches")
+        _check(lib.pkv_paged_attn_decode_window(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                                _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, D, BS, NB,
+                                                block_tables.shape[1], int(max_seq_len), float(scale),
+                                                int(window), int(partition_tokens), _ptr(workspace), wbytes,
+                                                _stream(q)), "paged_attn_decode_window")
+        return out
     if fp8:
         _check(lib.pkv_paged_attn_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                              _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, D, BS, NB,
@@ -364,4 +382,41 @@ def swap_blocks(src: torch.Tensor, dst: torch.Tensor, block_mapping) -> None:
                                ctypes.c_void_p(m.data_ptr()) if m.numel() else None, m.shape[0],
                                _block_bytes(src) if src.shape[0] else _block_bytes(dst), src.shape[0],
                                dst.shape[0], _stream(dev_t)), "swap_blocks")
+
+
+class StreamedDecode:
+    """Decode attention streamed over tiles of resident blocks (pkv_stream_attn_*): begin(), then
+    step(tile_tables, tile_lens) once per tile (any order), then finalize() -> out [B, Hq, D].
+    Owns its state buffer (allocated once with torch)."""
+
+    def __init__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, scale: float):
+        _need(q, "q", torch.bfloat16, 3, q.device)
+        _need(k_cache, "k_cache", torch.bfloat16, 4, q.device)
+        _need(v_cache, "v_cache", torch.bfloat16, 4, q.device)
+        self.q, self.k_cache, self.v_cache, self.scale = q, k_cache, v_cache, float(scale)
+        B, Hq, D = q.shape
+        self.nbytes = int(load_library().pkv_stream_attn_state_bytes(B, Hq, D))
+        self.state = torch.empty(max(self.nbytes, 16), dtype=torch.uint8, device=q.device)
+
+    def begin(self):
+        B, Hq, D = self.q.shape
+        _check(load_library().pkv_stream_attn_begin(_ptr(self.state), self.nbytes, B, Hq, D, _stream(self.q)),
+               "stream_attn_begin")
+
+    def step(self, tile_tables: torch.Tensor, tile_lens: torch.Tensor):
+        B, Hq, D = self.q.shape
+        NB, Hkv, BS, _ = self.k_cache.shape
+        _need(tile_tables, "tile_tables", torch.int32, 2, self.q.device)
+        _need(tile_lens, "tile_lens", torch.int32, 1, self.q.device)
+        _check(load_library().pkv_stream_attn_step(_ptr(self.q), _ptr(self.k_cache), _ptr(self.v_cache),
+                                                   _ptr(tile_tables), _ptr(tile_lens), _ptr(self.state),
+                                                   self.nbytes, B, Hq, Hkv, D, BS, NB, tile_tables.shape[1],
+                                                   self.scale, _stream(self.q)), "stream_attn_step")
+
+    def finalize(self, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+        B, Hq, D = self.q.shape
+        out = torch.empty_like(self.q) if out is None else out
+        _check(load_library().pkv_stream_attn_finalize(_ptr(self.state), self.nbytes, _ptr(out), _ptr(lse),
+                                                       B, Hq, D, _stream(self.q)), "stream_attn_finalize")
+        return out
 

@@ -102,7 +102,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
                        int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                        int32_t max_seq_len, float scale, int32_t partition_tokens, void* workspace,
                        size_t workspace_bytes, int kv_fp8, float k_scale, float v_scale,
-                       void* stream) {
+                       int window, void* stream) {
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_seq_len < 0 || partition_tokens < -1)
     return PKV_E_INVALID_ARGUMENT;
@@ -138,6 +138,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.kv_fp8 = kv_fp8;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.window = window;
   a.partition_tokens =
       resolve_partition(batch, num_q_heads, num_kv_heads, max_seq_len, partition_tokens);
   if (a.partition_tokens > 0) {
@@ -168,7 +169,7 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
   return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                      max_seq_len, scale, partition_tokens, workspace, workspace_bytes, 0, 1.f, 1.f,
-                     stream);
+                     0, stream);
 }
 
 int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -182,7 +183,103 @@ int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_
   return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                      max_seq_len, scale, partition_tokens, workspace, workspace_bytes, 1, k_scale,
-                     v_scale, stream);
+                     v_scale, 0, stream);
+}
+
+int pkv_paged_attn_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                                 float* lse, int32_t batch, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, int32_t max_blocks_per_seq,
+                                 int32_t max_seq_len, float scale, int32_t window,
+                                 int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (window < 0) return PKV_E_INVALID_ARGUMENT;
+  return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                     max_seq_len, scale, partition_tokens, workspace, workspace_bytes, 0, 1.f, 1.f,
+                     window, stream);
+}
+
+static pkv::DecodeWorkspaceLayout stream_state_layout(int batch, int num_q_heads, int head_dim) {
+  // one partition per (sequence, q head): o [B, 1, Hq, D], m and l [B, 1, Hq]
+  return pkv::decode_workspace_layout(batch, num_q_heads, head_dim, 1, 1);
+}
+
+size_t pkv_stream_attn_state_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim) {
+  if (batch <= 0 || num_q_heads <= 0 || !head_dim_ok(head_dim)) return 0;
+  return stream_state_layout(batch, num_q_heads, head_dim).total;
+}
+
+int pkv_stream_attn_begin(void* state, size_t state_bytes, int32_t batch, int32_t num_q_heads,
+                          int32_t head_dim, void* stream) {
+  if (batch < 0 || num_q_heads <= 0) return PKV_E_INVALID_ARGUMENT;
+  if (!head_dim_ok(head_dim)) return PKV_E_UNSUPPORTED;
+  if (batch == 0) return PKV_OK;
+  const pkv::DecodeWorkspaceLayout l = stream_state_layout(batch, num_q_heads, head_dim);
+  if (!state || !aligned16(state)) return PKV_E_INVALID_ARGUMENT;
+  if (state_bytes < l.total) return PKV_E_WORKSPACE_TOO_SMALL;
+  char* st = static_cast<char*>(state);
+  return hip_status(pkv::launch_stream_state_begin(
+      reinterpret_cast<float*>(st + l.o_off), reinterpret_cast<float*>(st + l.m_off),
+      reinterpret_cast<float*>(st + l.l_off), batch * num_q_heads, head_dim, (hipStream_t)stream));
+}
+
+int pkv_stream_attn_step(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* tile_tables, const int32_t* tile_lens, void* state,
+                         size_t state_bytes, int32_t batch, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, int32_t tile_capacity, float scale, void* stream) {
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || tile_capacity <= 0)
+    return PKV_E_INVALID_ARGUMENT;
+  if (num_q_heads % num_kv_heads != 0) return PKV_E_INVALID_ARGUMENT;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PKV_E_UNSUPPORTED;
+  if (batch == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !tile_tables || !tile_lens || !state) return PKV_E_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(state))
+    return PKV_E_INVALID_ARGUMENT;
+  const int G = num_q_heads / num_kv_heads;
+  if (batch > 65535 || (long)num_kv_heads * ((G + 15) / 16) > 65535) return PKV_E_UNSUPPORTED;
+  const pkv::DecodeWorkspaceLayout l = stream_state_layout(batch, num_q_heads, head_dim);
+  if (state_bytes < l.total) return PKV_E_WORKSPACE_TOO_SMALL;
+  char* st = static_cast<char*>(state);
+  pkv::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = tile_tables;
+  a.seq_lens = tile_lens;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = tile_capacity;
+  a.max_seq_len = tile_capacity * block_size;
+  a.scale = scale;
+  a.k_scale = a.v_scale = 1.f;
+  a.partition_tokens = 0;  // one direct pass over the tile, folded into the state
+  a.o_part = reinterpret_cast<float*>(st + l.o_off);
+  a.m_part = reinterpret_cast<float*>(st + l.m_off);
+  a.l_part = reinterpret_cast<float*>(st + l.l_off);
+  return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+int pkv_stream_attn_finalize(const void* state, size_t state_bytes, void* out, float* lse,
+                             int32_t batch, int32_t num_q_heads, int32_t head_dim, void* stream) {
+  if (batch < 0 || num_q_heads <= 0) return PKV_E_INVALID_ARGUMENT;
+  if (!head_dim_ok(head_dim)) return PKV_E_UNSUPPORTED;
+  if (batch == 0) return PKV_OK;
+  if (!state || !out || !aligned16(state) || !aligned16(out)) return PKV_E_INVALID_ARGUMENT;
+  const pkv::DecodeWorkspaceLayout l = stream_state_layout(batch, num_q_heads, head_dim);
+  if (state_bytes < l.total) return PKV_E_WORKSPACE_TOO_SMALL;
+  const char* st = static_cast<const char*>(state);
+  return hip_status(pkv::launch_stream_state_finalize(
+      reinterpret_cast<const float*>(st + l.o_off), reinterpret_cast<const float*>(st + l.m_off),
+      reinterpret_cast<const float*>(st + l.l_off), out, lse, batch * num_q_heads, head_dim,
+      (hipStream_t)stream));
 }
 
 int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -24,6 +24,8 @@
 //   * slots past the sequence length are masked by selection (their bits may be NaN).
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "common.h"
@@ -73,7 +75,7 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
               float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ m_part,
               float* __restrict__ l_part, int Hq, int Hkv, int G, int n_hg, int BS, int NB,
               int max_blocks, int PT, int Pmax, float scale_log2, float v_scale, int negate_q,
-              int bs_shift) {
+              int bs_shift, int window) {
   using C = DecodeCfg<D>;
   using Chunk = DecodeChunk<D, FP8>;
   using KVT = std::conditional_t<FP8, uint8_t, uint16_t>;
@@ -92,12 +94,14 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
   const int qg = lane >> 4;   // lane group 0..3
 
   int L = clampi(lens[b], 0, max_blocks * BS);
-  int t_begin = 0, t_end = L;
+  if constexpr (SPLIT) L = min(L, Pmax * PT);
+  // sliding window: keys [t_lo, L); chunks stay 32-token aligned, keys before t_lo are masked
+  const int t_lo = window > 0 ? max(0, L - window) : 0;
+  int t_begin = t_lo & ~31, t_end = L;
   if constexpr (SPLIT) {
-    L = min(L, Pmax * PT);
-    t_begin = p * PT;
-    if (t_begin >= L) return;  // uniform over the work-group
-    t_end = min(L, t_begin + PT);
+    t_begin = max(p * PT, t_begin);
+    t_end = min(L, p * PT + PT);
+    if (t_begin >= t_end) return;  // uniform over the work-group (no partial is written)
   }
 
   const int gcol = hg * 16 + col;
@@ -161,7 +165,8 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
 
   auto process = [&](const Chunk& ch, int c) {
     const int cs = t_begin + c * 32;
-    const bool partial = cs + 31 > last;  // only a partition's last chunk can hold slack rows
+    // only a partition's last chunk holds slack rows, only a window's first one keys before t_lo
+    const bool partial = cs + 31 > last || cs < t_lo;
     // S^T[token][head] for the two half pages
     f32x4 s[2];
 #pragma unroll
@@ -189,7 +194,8 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
           const int u = i * 64 + lane;
           const int row = u / (D / 8);
           u32x4 val = piece_bf16(ch.v[hh][i]);
-          if (cs + 16 * hh + row > last) val = u32x4{0, 0, 0, 0};
+          const int tok = cs + 16 * hh + row;
+          if (tok > last || tok < t_lo) val = u32x4{0, 0, 0, 0};
           *reinterpret_cast<u32x4*>(vbuf + (16 * hh + row) * C::RS + (u - row * (D / 8)) * 16) = val;
         }
     }
@@ -201,8 +207,10 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
       for (int r = 0; r < 4; ++r) sv[hh * 4 + r] = s[hh][r];
     if (partial) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (cs + 16 * (j >> 2) + 4 * qg + (j & 3) > last) sv[j] = -INFINITY;
+      for (int j = 0; j < 8; ++j) {
+        const int tok = cs + 16 * (j >> 2) + 4 * qg + (j & 3);
+        if (tok > last || tok < t_lo) sv[j] = -INFINITY;
+      }
     }
     float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
@@ -343,6 +351,29 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
         m_part[pi] = M;
         l_part[pi] = lsum;
       }
+    } else if (o_part != nullptr) {
+      // streamed attention: fold this launch's (max, exp-sum, normalised output) into the running
+      // state of (b, hout). The column's threads are one wave: every lane reads before any writes.
+      const size_t si = (size_t)b * Hq + hout;
+      const float ms = m_part[si];
+      const float ls = l_part[si];
+      const float Mn = fmaxf(ms, M);
+      const float ws = (ms == -INFINITY) ? 0.f : ls * fast_exp2(ms - Mn);
+      const float wp = (M == -INFINITY) ? 0.f : lsum * fast_exp2(M - Mn);
+      const float tot = ws + wp;
+      const float as = tot > 0.f ? ws / tot : 0.f;
+      const float ap = tot > 0.f ? wp / tot : 0.f;
+      float* op = o_part + si * D + dpart * DPT;
+#pragma unroll
+      for (int i = 0; i < DPT; i += 4) {
+        const f32x4 old = *reinterpret_cast<const f32x4*>(op + i);
+        *reinterpret_cast<f32x4*>(op + i) =
+            old * as + f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]} * ap;
+      }
+      if (dpart == 0) {
+        m_part[si] = tot > 0.f ? Mn : -INFINITY;
+        l_part[si] = tot;
+      }
     } else {
       uint16_t* op = out + ((size_t)b * Hq + hout) * D + dpart * DPT;
 #pragma unroll
@@ -355,6 +386,34 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
   }
 }
 
+// Streamed attention state [B, Hq]: normalised output rows o (fp32, D), running max m (log2 units)
+// and exp-sum l. begin: o = 0, m = -inf, l = 0 (a fill kernel, safe inside a captured graph).
+__global__ void __launch_bounds__(256)
+stream_state_begin_kernel(float* __restrict__ o, float* __restrict__ m, float* __restrict__ l,
+                          int64_t rows, int D) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows * D; i += stride) {
+    o[i] = 0.f;
+    if (i < rows) {
+      m[i] = -INFINITY;
+      l[i] = 0.f;
+    }
+  }
+}
+
+// finalize: out = bf16(o) (already normalised; zero rows for an empty state), lse in natural log
+__global__ void __launch_bounds__(256)
+stream_state_finalize_kernel(const float* __restrict__ o, const float* __restrict__ m,
+                             const float* __restrict__ l, uint16_t* __restrict__ out,
+                             float* __restrict__ lse, int64_t rows, int D) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows * D / 2; i += stride) {
+    const float2 v = reinterpret_cast<const float2*>(o)[i];
+    reinterpret_cast<uint32_t*>(out)[i] = pack_bf16x2(v.x, v.y);
+    if (lse != nullptr && i < rows) lse[i] = l[i] > 0.f ? (m[i] + __log2f(l[i])) * kLn2 : -INFINITY;
+  }
+}
+
 // Log-sum-exp merge of split partials: one work-group per (q head, sequence). Thread group g
 // (U threads, one float4 of the row each) folds partitions g, g+NG, ... into a running
 // (max, exp-sum, weighted output), loading kMergeUnroll partitions at a time; the NG group states
@@ -364,7 +423,7 @@ __global__ void __launch_bounds__(NT)
 decode_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ m_part,
                     const float* __restrict__ l_part, const int32_t* __restrict__ lens,
                     uint16_t* __restrict__ out, float* __restrict__ lse, int Hq, int max_blocks,
-                    int BS, int PT, int Pmax) {
+                    int BS, int PT, int Pmax, int window) {
   constexpr int U = D / 4;    // float4 units per partial row
   constexpr int NG = NT / U;  // partition groups
   __shared__ float sm[NG];
@@ -376,6 +435,8 @@ decode_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ 
   int L = clampi(lens[b], 0, max_blocks * BS);
   L = min(L, Pmax * PT);
   const int P = (L + PT - 1) / PT;  // partitions holding tokens (each has a finite max)
+  // a sliding window leaves the partitions before its first key unwritten
+  const int p_lo = window > 0 ? max(0, L - window) / PT : 0;
   // partial p of (b, h) is row (b * Pmax + p) * Hq + h
   const size_t pi0 = (size_t)b * Pmax * Hq + h;
   const int u = t % U;
@@ -384,7 +445,7 @@ decode_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ 
   float Mg = -INFINITY;  // log2 units
   float Sg = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int p0 = g; p0 < P; p0 += NG * kMergeUnroll) {
+  for (int p0 = p_lo + g; p0 < P; p0 += NG * kMergeUnroll) {
     f32x4 x[kMergeUnroll];
     float mp[kMergeUnroll], lp[kMergeUnroll];
 #pragma unroll
@@ -476,7 +537,7 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
                        a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, a.o_part, a.m_part,
                        a.l_part, a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size,
                        a.num_blocks, a.max_blocks_per_seq, a.partition_tokens, a.max_partitions,
-                       scale_log2, v_scale, negate_q, bs_shift);
+                       scale_log2, v_scale, negate_q, bs_shift, a.window);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // long splits take 1024 threads per (head, sequence), so one batch of loads covers them
@@ -484,19 +545,22 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     if (a.max_partitions > 4 * kMergeUnroll)
       hipLaunchKernelGGL((decode_merge_kernel<D, 1024>), mgrid, dim3(1024), 0, stream, a.o_part,
                          a.m_part, a.l_part, a.seq_lens, (uint16_t*)a.out, a.lse, a.num_q_heads,
-                         a.max_blocks_per_seq, a.block_size, a.partition_tokens, a.max_partitions);
+                         a.max_blocks_per_seq, a.block_size, a.partition_tokens, a.max_partitions,
+                         a.window);
     else
       hipLaunchKernelGGL((decode_merge_kernel<D, 256>), mgrid, dim3(256), 0, stream, a.o_part,
                          a.m_part, a.l_part, a.seq_lens, (uint16_t*)a.out, a.lse, a.num_q_heads,
-                         a.max_blocks_per_seq, a.block_size, a.partition_tokens, a.max_partitions);
+                         a.max_blocks_per_seq, a.block_size, a.partition_tokens, a.max_partitions,
+                         a.window);
     return hipGetLastError();
   }
+  // direct path; with a stream state (o_part etc. set, no partitions) the result is folded into it
   const dim3 grid(1, a.num_kv_heads * n_hg, a.batch);
   hipLaunchKernelGGL((decode_kernel<D, kDirectWaves, false, FP8>), grid, dim3(kDirectWaves * kWave),
                      0, stream, (const uint16_t*)a.q, (const KVT*)a.k_cache, (const KVT*)a.v_cache,
-                     a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, nullptr, nullptr, nullptr,
-                     a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size, a.num_blocks,
-                     a.max_blocks_per_seq, 0, 1, scale_log2, v_scale, negate_q, bs_shift);
+                     a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, a.o_part, a.m_part,
+                     a.l_part, a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size, a.num_blocks,
+                     a.max_blocks_per_seq, 0, 1, scale_log2, v_scale, negate_q, bs_shift, a.window);
   return hipGetLastError();
 }
 
@@ -508,6 +572,26 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     case 256: return launch_decode_d<256, FP8>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_stream_state_begin(float* o, float* m, float* l, int rows, int head_dim,
+                                     hipStream_t stream) {
+  const int64_t n = (int64_t)rows * head_dim;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(stream_state_begin_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o, m, l,
+                     (int64_t)rows, head_dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_state_finalize(const float* o, const float* m, const float* l, void* out,
+                                        float* lse, int rows, int head_dim, hipStream_t stream) {
+  const int64_t n = (int64_t)rows * head_dim / 2;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(stream_state_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o, m,
+                     l, (uint16_t*)out, lse, (int64_t)rows, head_dim);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

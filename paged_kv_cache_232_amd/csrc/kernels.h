@@ -27,12 +27,18 @@ struct DecodeArgs {
   int partition_tokens;  // 0 = direct, > 0 = split
   int kv_fp8;            // caches hold fp8 (e4m3) codes dequantised by k_scale / v_scale
   float k_scale, v_scale;
+  int window;            // > 0: keys [L - window, L) only
   // split workspace (null for direct)
   float* o_part;
   float* m_part;
   float* l_part;
   int max_partitions;
 };
+
+hipError_t launch_stream_state_begin(float* o, float* m, float* l, int rows, int head_dim,
+                                     hipStream_t stream);
+hipError_t launch_stream_state_finalize(const float* o, const float* m, const float* l, void* out,
+                                        float* lse, int rows, int head_dim, hipStream_t stream);
 
 // Split-KV workspace layout for a given shape: o [B, P, Hq, D] f32, m and l [B, P, Hq] f32, each
 // region 256-byte aligned.

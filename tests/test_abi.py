@@ -24,7 +24,7 @@ def _declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = pkv.load_library()
     syms = _declared_symbols()
-    assert len(syms) == 12, syms
+    assert len(syms) == 17, syms
     for s in syms:
         assert hasattr(lib, s), f"{s} missing from libpkv.so"
     assert set(syms) == set(pkv._SIGNATURES), "binding and header disagree"
