@@ -10,8 +10,9 @@ One step runs every call of the hot path once, on inputs already resident in HBM
 Each call is bracketed by HIP events on the stream it is launched on. The headline value is the
 decode KV bandwidth (algorithmic bytes of calls 3 and 4 over their measured time); the ragged
 prefill TFLOP/s is reported beside it. The direct and split decode paths of workload 3, decode of
-workloads 3 and 4 over an fp8 (e4m3) cache, a small decode step (eager and replayed from a HIP
-graph), and the block-management calls (copy_blocks over 32 layers, swap_blocks to pinned host
+workloads 3 and 4 over an fp8 (e4m3) cache, a sliding window over workload 4, workload 3 streamed
+over tiles of resident blocks, a small decode step (eager and replayed from a HIP graph), and the
+block-management calls (copy_blocks over 32 layers, swap_blocks to pinned host
 memory) are timed separately, outside the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -194,6 +195,41 @@ def build_cases(dev):
                                            "GB/s")
             cases["decode3_split"] = Case("paged_attn_decode split 512 (batched decode)", mk(c, 512), "hbm", work,
                                           "GB/s")
+        if cid == 4:
+            # sliding window of the last 8192 tokens over the long contexts (split 512)
+            W = 8192
+            wlens = [min(L, W) for L in lens]
+
+            def mkw(c=c):
+                return lambda: pkv.paged_attn_decode(c["q"], c["kc"], c["vc"], c["bt"], c["sl"], c["scale"],
+                                                     max_seq_len=c["msl"], partition_tokens=512, out=c["out"],
+                                                     workspace=c["ws"], window=W)
+            cases["decode4_window"] = Case(f"paged_attn_decode_window (long-context, window {W}, split 512)",
+                                           mkw(), "hbm", decode_bytes(wlens, Hq, Hkv, D, di.block_size), "GB/s")
+        if cid == 3:
+            # the batched workload streamed over tiles of 64 resident blocks (1024 tokens): one
+            # launch per tile folded into a running state, then finalize
+            cap = 64
+            ntile = -(-max(lens) // (cap * di.block_size))
+            tiles = []
+            for i in range(ntile):
+                t_tab = torch.zeros((B, cap), dtype=torch.int32)
+                t_len = torch.zeros(B, dtype=torch.int32)
+                for b_, L in enumerate(lens):
+                    nblk = -(-L // di.block_size)
+                    blocks = di.block_tables[b_, i * cap:min((i + 1) * cap, nblk)]
+                    t_tab[b_, :len(blocks)] = blocks
+                    t_len[b_] = max(0, min(L - i * cap * di.block_size, cap * di.block_size))
+                tiles.append((t_tab.to(dev), t_len.to(dev)))
+            sdec = pkv.StreamedDecode(c["q"], c["kc"], c["vc"], c["scale"])
+
+            def streamed(sdec=sdec, tiles=tiles, c=c):
+                sdec.begin()
+                for t_tab, t_len in tiles:
+                    sdec.step(t_tab, t_len)
+                sdec.finalize(out=c["out"])
+            cases["decode3_streamed"] = Case(f"streamed decode, batched workload over {ntile} tiles of {cap} blocks",
+                                             streamed, "hbm", work, "GB/s")
         # the same workload over an fp8 (e4m3) cache (timed alone): codes of cache / scale, one byte
         # per element, so half the bytes of the bf16 cache
         c["k_scale"], c["v_scale"] = 0.02, 0.02
@@ -266,8 +302,8 @@ def build_cases(dev):
 
 STEP = ["scatter5", "paged5", "ragged2", "decode3", "decode4"]
 # timed alone, outside the step
-EXTRA = ["decode3_direct", "decode3_split", "decode3_fp8", "decode4_fp8", "decode_step_eager", "decode_step_graph",
-         "copy_blocks", "swap_out"]
+EXTRA = ["decode3_direct", "decode3_split", "decode3_fp8", "decode4_fp8", "decode4_window", "decode3_streamed",
+         "decode_step_eager", "decode_step_graph", "copy_blocks", "swap_out"]
 
 
 def time_step(cases, steps, warmup):
