@@ -630,14 +630,11 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
-// head dims that run the 16-row form
+// head dims that run the 16-row form (at head_dim <= 128 the 32-row form is faster: two waves per
+// SIMD fit either way, and it reads half the LDS bytes per FLOP)
 template <int D>
 constexpr bool use_p16() {
-#ifdef PKV_P16_ALL
-  return true;
-#else
   return D >= 256;
-#endif
 }
 
 template <int D, bool PAGED>
