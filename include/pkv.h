@@ -125,6 +125,8 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
  *   k, v     [kv_indptr_h[batch], num_kv_heads, head_dim] bf16.
  *   qo_indptr, kv_indptr        device [batch + 1] int32 prefix sums (read by the kernel).
  *   qo_indptr_h, kv_indptr_h    host copies of the same (sizes the launch; no device sync).
+ * PKV_E_UNSUPPORTED for head_dim other than 64/128/256 or num_kv_heads * head_dim >= 2^23 (also
+ * for pkv_paged_prefill).
  */
 int pkv_ragged_prefill(const void* q, const void* k, const void* v, void* out,
                        const int32_t* qo_indptr, const int32_t* kv_indptr,

@@ -305,6 +305,8 @@ static int check_prefill_common(const void* q, const void* out, const int32_t* q
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0) return PKV_E_INVALID_ARGUMENT;
   if (num_q_heads % num_kv_heads != 0) return PKV_E_INVALID_ARGUMENT;
   if (!head_dim_ok(head_dim)) return PKV_E_UNSUPPORTED;
+  // the kernels form a tile's per-lane K/V offsets with 24-bit multiplies of the row stride
+  if ((int64_t)num_kv_heads * head_dim >= (1 << 23)) return PKV_E_UNSUPPORTED;
   if (batch == 0) {
     *max_qo = 0;
     *total_q = 0;

@@ -111,6 +111,34 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Raw buffer resource over memory starting at a wave-uniform address (no bounds limit: callers
+// keep every offset inside their tensors). Loads through it take a 32-bit per-lane byte offset,
+// so a tile's addresses cost one VALU op per unit instead of a 64-bit add per load.
+// The address is made explicitly uniform (the compiler would otherwise loop over lanes whenever
+// it cannot prove that itself).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_at(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                     ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0, -1, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// acc + the sum of 8 bf16 values (two per v_dot2_f32_bf16 against (1, 1); the products are exact)
+__device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
+  const u32x4 u = __builtin_bit_cast(u32x4, p);
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // copied out first: a bit_cast applied directly to a vector element reads element 0
+    const uint32_t x = u[i];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
+  }
+  return acc;
+}
+
 __device__ __forceinline__ u32x2 load8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }

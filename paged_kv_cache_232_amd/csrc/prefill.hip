@@ -170,7 +170,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int last_n0 = (n_kt - 1) * C::BN;  // first row of the last tile
   auto fetch = [&](int n0, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
-    n0 = min(n0, last_n0);           // loads past the last tile repeat it
+    n0 = __builtin_amdgcn_readfirstlane(min(n0, last_n0));  // past the last tile: repeat it
     const int last_r = kv - 1 - n0;  // >= 0: the tile's last row inside the request
 #pragma unroll
     for (int i = 0; i < C::UPT; ++i) {
@@ -178,19 +178,19 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const int rr = u / C::UPR;
       const int cu = u - rr * C::UPR;
       const int r = min(rr, last_r);
-      size_t base;  // wave-uniform
-      int off;      // per lane
+      size_t base;  // wave-uniform element offset
+      int off;      // per-lane byte offset
       if constexpr (PAGED) {
         // the instruction's first row: wave-uniform, in the same block as every row it loads
         const int nb = min(n0 + (i * kPrefillThreads + w_u0) / C::UPR, kv - 1);
         base = pl.block_offset(nb);
-        off = ((n0 + r) & (BS - 1)) * D + cu * 8;
+        off = (__umul24((n0 + r) & (BS - 1), D) + cu * 8) * 2;  // 24-bit products (host-checked)
       } else {
         base = rl.row_offset(n0);
-        off = r * (Hkv * D) + cu * 8;
+        off = (__umul24(r, Hkv * D) + cu * 8) * 2;
       }
-      kpre[sl][i] = load16(k + base + off);
-      vpre[sl][i] = load16(v + base + off);
+      kpre[sl][i] = buffer_load16(buffer_at(k + base), off);
+      vpre[sl][i] = buffer_load16(buffer_at(v + base), off);
       memory_order_point();
     }
   };
@@ -285,9 +285,9 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       for (int j = 0; j < 8; ++j) {
         const float e = fast_exp2(__builtin_fmaf(s[st >> 1][8 * (st & 1) + j], scale_log2, neg_m));
         pv[j] = e;
-        ps += e;
       }
       pb[st] = pack_bf16x8(pv);
+      ps = sum_bf16x8(pb[st], ps);  // the sum of the probabilities PV actually uses
     }
     l_run += ps;
 
@@ -464,7 +464,7 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int last_n0 = (n_kt - 1) * C::BN;  // first row of the last tile
   auto fetch = [&](int n0, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
-    n0 = min(n0, last_n0);           // loads past the last tile repeat it
+    n0 = __builtin_amdgcn_readfirstlane(min(n0, last_n0));  // past the last tile: repeat it
     const int last_r = kv - 1 - n0;  // >= 0: the tile's last row inside the request
 #pragma unroll
     for (int i = 0; i < C::UPT; ++i) {
@@ -472,19 +472,19 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const int rr = u / C::UPR;
       const int cu = u - rr * C::UPR;
       const int r = min(rr, last_r);
-      size_t base;  // wave-uniform
-      int off;      // per lane
+      size_t base;  // wave-uniform element offset
+      int off;      // per-lane byte offset
       if constexpr (PAGED) {
         // the instruction's first row: wave-uniform, in the same block as every row it loads
         const int nb = min(n0 + (i * kP16Threads + w_u0) / C::UPR, kv - 1);
         base = pl.block_offset(nb);
-        off = ((n0 + r) & (BS - 1)) * D + cu * 8;
+        off = (__umul24((n0 + r) & (BS - 1), D) + cu * 8) * 2;  // 24-bit products (host-checked)
       } else {
         base = rl.row_offset(n0);
-        off = r * (Hkv * D) + cu * 8;
+        off = (__umul24(r, Hkv * D) + cu * 8) * 2;
       }
-      kpre[sl][i] = load16(k + base + off);
-      vpre[sl][i] = load16(v + base + off);
+      kpre[sl][i] = buffer_load16(buffer_at(k + base), off);
+      vpre[sl][i] = buffer_load16(buffer_at(v + base), off);
       memory_order_point();
     }
   };
@@ -570,9 +570,9 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           const float e =
               fast_exp2(__builtin_fmaf(s[2 * st + (j >> 2)][j & 3], scale_log2, neg_m));
           pv[j] = e;
-          ps += e;
         }
         pb[st] = pack_bf16x8(pv);
+        ps = sum_bf16x8(pb[st], ps);
       }
       l_run += ps;
 #pragma unroll

@@ -30,6 +30,9 @@ RAGGED_EDGE = [
     ([257, 64], None, 16, 4, 256, True),            # head_dim 256
     ([40, 0, 77], [60, 5, 77], 8, 2, 128, True),    # an empty request
     ([300], [0], 2, 1, 64, False),                  # no keys at all
+    ([513, 255, 256], None, 4, 1, 128, True),       # several 256-row q tiles, ragged tails
+    ([700, 31], [1500, 31], 2, 2, 64, True),        # long prefix offset, head_dim 64
+    ([600, 90], [600, 4000], 4, 2, 128, False),     # non-causal, kv much longer than q
 ]
 
 
@@ -68,6 +71,7 @@ PAGED_EDGE = [
     ([9, 200], [300, 0], 8, 2, 256, 16),
     ([50, 129], [16, 100], 4, 1, 128, 32),
     ([33], [5000], 2, 2, 64, 64),
+    ([600, 257], [700, 0], 4, 2, 128, 16),
 ]
 
 
