@@ -358,6 +358,8 @@ int pkv_ragged_prefill(const void* q, const void* k, const void* v, void* out,
   a.head_dim = head_dim;
   a.causal = causal != 0;
   a.scale = scale;
+  a.qo_indptr_h = qo_indptr_h;
+  a.kv_indptr_h = kv_indptr_h;
   a.max_qo_len = max_qo;
   a.total_q = total_q;
   a.total_kv = total_kv;
@@ -403,6 +405,8 @@ int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.causal = causal != 0;
   a.scale = scale;
+  a.qo_indptr_h = qo_indptr_h;
+  a.kv_lens_h = kv_lens_h;
   a.max_qo_len = max_qo;
   a.total_q = total_q;
   const hipError_t e = pkv::launch_paged_prefill(a, (hipStream_t)stream);

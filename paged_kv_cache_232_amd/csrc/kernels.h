@@ -64,6 +64,9 @@ struct PrefillArgs {
   int block_size, num_blocks, max_blocks_per_seq;  // paged only
   int causal;
   float scale;
+  const int32_t* qo_indptr_h;   // host copies (order the work-groups; may be null)
+  const int32_t* kv_indptr_h;   // ragged only
+  const int32_t* kv_lens_h;     // paged only
   int max_qo_len;   // host-side maximum of the q lengths (sizes the grid)
   int total_q;      // rows of q / out
   int64_t total_kv; // rows of k / v (ragged only)

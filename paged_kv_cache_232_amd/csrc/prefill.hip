@@ -21,12 +21,23 @@
 //   * q tiles are issued last-first (the longest causal rows start first).
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
+#include <vector>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace pkv {
+
+// Work-group schedule: entry y of the grid's y dimension is (request << 16 | q tile), sorted by
+// decreasing visible keys, so the hardware dispatcher starts the longest work first (greedy
+// longest-first list scheduling). n == 0: the plain (request, last-tile-first) grid instead.
+constexpr int kMaxOrder = 768;
+struct TileOrder {
+  int32_t n;
+  uint32_t e[kMaxOrder];
+};
 
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
@@ -93,7 +104,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
                const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ tables,
                int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
-               int negate_q, int xcd_heads, int bs_shift) {
+               int negate_q, int xcd_heads, int bs_shift, const TileOrder order) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
   // buffer j (0/1): K rows at smem + j*BUF, V rows BN*RSE further
@@ -101,7 +112,8 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // block x -> q head: heads sharing a kv head go to the same XCD (round-robin x % 8)
   int h = blockIdx.x;
   if (xcd_heads > 0) h = (blockIdx.x & 7) * xcd_heads + (blockIdx.x >> 3);
-  const int b = blockIdx.y;
+  const uint32_t sched = order.n > 0 ? order.e[min((int)blockIdx.y, kMaxOrder - 1)] : 0u;
+  const int b = order.n > 0 ? (int)(sched >> 16) : (int)blockIdx.y;
   const int G = Hq / Hkv;
   const int kh = h / G;
 
@@ -116,8 +128,9 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     kv = kv_indptr[b + 1] - (int)kv0;
   }
   const int n_qt = (qo + kBM - 1) / kBM;
-  const int qt = n_qt - 1 - (int)blockIdx.z;  // last tile first
-  if (qt < 0) return;
+  // scheduled tile, or the plain grid's last tile first
+  const int qt = order.n > 0 ? (int)(sched & 0xffffu) : n_qt - 1 - (int)blockIdx.z;
+  if (qt < 0 || qt >= n_qt) return;
   const int m0 = qt * kBM;
   const int off = kv - qo;  // row i sits at key position i + off
 
@@ -393,14 +406,15 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
                  const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ tables,
                  int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
-                 int negate_q, int xcd_heads, int bs_shift) {
+                 int negate_q, int xcd_heads, int bs_shift, const TileOrder order) {
   using C = P16Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
   // buffer j (0/1): K rows at smem + j*BUF, V rows BN*RSE further; the output tile reuses it
 
   int h = blockIdx.x;
   if (xcd_heads > 0) h = (blockIdx.x & 7) * xcd_heads + (blockIdx.x >> 3);
-  const int b = blockIdx.y;
+  const uint32_t sched = order.n > 0 ? order.e[min((int)blockIdx.y, kMaxOrder - 1)] : 0u;
+  const int b = order.n > 0 ? (int)(sched >> 16) : (int)blockIdx.y;
   const int G = Hq / Hkv;
   const int kh = h / G;
 
@@ -415,8 +429,9 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     kv = kv_indptr[b + 1] - (int)kv0;
   }
   const int n_qt = (qo + kP16BM - 1) / kP16BM;
-  const int qt = n_qt - 1 - (int)blockIdx.z;  // last tile first
-  if (qt < 0) return;
+  // scheduled tile, or the plain grid's last tile first
+  const int qt = order.n > 0 ? (int)(sched & 0xffffu) : n_qt - 1 - (int)blockIdx.z;
+  if (qt < 0 || qt >= n_qt) return;
   const int m0 = qt * kP16BM;
   const int off = kv - qo;  // row i sits at key position i + off
 
@@ -637,29 +652,61 @@ constexpr bool use_p16() {
   return D >= 256;
 }
 
+// Longest-first schedule of the (request, q tile) work-groups from the host copies of the
+// lengths: work = keys a tile's rows can see. Empty when a copy is missing or there are more
+// tiles than the schedule holds.
+static void build_order(const PrefillArgs& a, TileOrder& ord) {
+  ord.n = 0;
+  if (a.qo_indptr_h == nullptr || (a.kv_indptr_h == nullptr && a.kv_lens_h == nullptr)) return;
+  struct Item {
+    int64_t work;
+    uint32_t e;
+  };
+  std::vector<Item> items;
+  for (int b = 0; b < a.batch; ++b) {
+    const int qo = a.qo_indptr_h[b + 1] - a.qo_indptr_h[b];
+    int64_t kv = a.kv_indptr_h ? (int64_t)a.kv_indptr_h[b + 1] - a.kv_indptr_h[b]
+                               : std::min<int64_t>(std::max(a.kv_lens_h[b], 0),
+                                                   (int64_t)a.max_blocks_per_seq * a.block_size);
+    const int n_qt = (qo + kBM - 1) / kBM;
+    if (n_qt > 0xffff || (int)items.size() + n_qt > kMaxOrder) return;
+    for (int qt = 0; qt < n_qt; ++qt) {
+      int64_t vis = kv;
+      if (a.causal) vis = std::min<int64_t>(kv, (int64_t)(qt + 1) * kBM + kv - qo);
+      items.push_back({std::max<int64_t>(vis, 0), ((uint32_t)b << 16) | (uint32_t)qt});
+    }
+  }
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& x, const Item& y) { return x.work > y.work; });
+  for (size_t i = 0; i < items.size(); ++i) ord.e[i] = items[i].e;
+  ord.n = (int)items.size();
+}
+
 template <int D, bool PAGED>
 static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
   const int n_qt = (a.max_qo_len + kBM - 1) / kBM;
   if (n_qt == 0) return hipSuccess;
+  TileOrder order;
+  build_order(a, order);
   const int xcd_heads = (a.num_q_heads % 8 == 0) ? a.num_q_heads / 8 : 0;
   float scale_log2 = a.scale * kLog2e;
   const int negate_q = scale_log2 < 0.f;
   if (negate_q) scale_log2 = -scale_log2;
   if (!(scale_log2 >= 1.17549435e-38f)) scale_log2 = 1.17549435e-38f;  // zero (or denormal) scale
-  const dim3 grid(a.num_q_heads, a.batch, n_qt);
+  const dim3 grid = order.n > 0 ? dim3(a.num_q_heads, order.n, 1) : dim3(a.num_q_heads, a.batch, n_qt);
   const int bs_shift = a.block_size > 0 ? __builtin_ctz((unsigned)a.block_size) : 0;
   if constexpr (use_p16<D>()) {
     hipLaunchKernelGGL((prefill16_kernel<D, PAGED>), grid, dim3(kP16Threads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
                        a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
-                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads, bs_shift);
+                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads, bs_shift, order);
   } else {
     hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(kPrefillThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
                        a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
-                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads, bs_shift);
+                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads, bs_shift, order);
   }
   return hipGetLastError();
 }

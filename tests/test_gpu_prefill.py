@@ -33,6 +33,7 @@ RAGGED_EDGE = [
     ([513, 255, 256], None, 4, 1, 128, True),       # several 256-row q tiles, ragged tails
     ([700, 31], [1500, 31], 2, 2, 64, True),        # long prefix offset, head_dim 64
     ([600, 90], [600, 4000], 4, 2, 128, False),     # non-causal, kv much longer than q
+    ([1] * 800, [37] * 800, 2, 1, 64, True),         # more q tiles than the launch schedule holds
 ]
 
 
