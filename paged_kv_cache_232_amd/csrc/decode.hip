@@ -75,7 +75,7 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
               float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ m_part,
               float* __restrict__ l_part, int Hq, int Hkv, int G, int n_hg, int BS, int NB,
               int max_blocks, int PT, int Pmax, float scale_log2, float v_scale, int negate_q,
-              int bs_shift, int window) {
+              int bs_shift, int window, int pair_order) {
   using C = DecodeCfg<D>;
   using Chunk = DecodeChunk<D, FP8>;
   using KVT = std::conditional_t<FP8, uint8_t, uint16_t>;
@@ -87,11 +87,28 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
   const int p = blockIdx.x;
   const int kh = blockIdx.y / n_hg;
   const int hg = blockIdx.y - kh * n_hg;
-  const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept scalar
   const int col = lane & 15;  // head column of the MFMA tiles
   const int qg = lane >> 4;   // lane group 0..3
+  int b = blockIdx.z;
+  if (pair_order) {
+    // Direct path, batch <= 64: work-group z takes the sequence of length rank z for z < B/2 and
+    // of rank B-1-(z-B/2) after, so the two work-groups the dispatcher places on one CU (z and
+    // z + B/2) pair a long sequence with a short one. Ties rank by index.
+    const int B = gridDim.z;
+    const int h = (B + 1) / 2;
+    const int target = (int)blockIdx.z < h ? (int)blockIdx.z : B - 1 - ((int)blockIdx.z - h);
+    int mine = -1;
+    if (lane < B) mine = clampi(lens[lane], 0, max_blocks * BS);
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+      const int lj = __builtin_amdgcn_readlane(mine, j);
+      rank += (lj > mine || (lj == mine && j < lane)) ? 1 : 0;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && rank == target);
+    b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+  }
 
   int L = clampi(lens[b], 0, max_blocks * BS);
   if constexpr (SPLIT) L = min(L, Pmax * PT);
@@ -537,7 +554,7 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
                        a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, a.o_part, a.m_part,
                        a.l_part, a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size,
                        a.num_blocks, a.max_blocks_per_seq, a.partition_tokens, a.max_partitions,
-                       scale_log2, v_scale, negate_q, bs_shift, a.window);
+                       scale_log2, v_scale, negate_q, bs_shift, a.window, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // long splits take 1024 threads per (head, sequence), so one batch of loads covers them
@@ -560,7 +577,8 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
                      0, stream, (const uint16_t*)a.q, (const KVT*)a.k_cache, (const KVT*)a.v_cache,
                      a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, a.o_part, a.m_part,
                      a.l_part, a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size, a.num_blocks,
-                     a.max_blocks_per_seq, 0, 1, scale_log2, v_scale, negate_q, bs_shift, a.window);
+                     a.max_blocks_per_seq, 0, 1, scale_log2, v_scale, negate_q, bs_shift, a.window,
+                     (a.batch <= 64 && a.o_part == nullptr) ? 1 : 0);
   return hipGetLastError();
 }
 
