@@ -37,6 +37,7 @@ constexpr int kDirectWaves = 4;  // waves per work-group on the direct path (spl
 constexpr float kRescaleLog2 = 8.0f;  // raise a running max only when exceeded by more than this
 constexpr int kPrefetch = 2;          // 32-token chunks per wave in flight (loads issued ahead)
 constexpr int kMergeUnroll = 8;       // merge: partial rows per thread in flight
+constexpr int kMaxStageBytes = 32 * 1024;  // split: LDS for parked partials per wave
 
 template <int D>
 struct DecodeCfg {
@@ -75,13 +76,17 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
               float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ m_part,
               float* __restrict__ l_part, int Hq, int Hkv, int G, int n_hg, int BS, int NB,
               int max_blocks, int PT, int Pmax, float scale_log2, float v_scale, int negate_q,
-              int bs_shift, int window, int pair_order) {
+              int bs_shift, int window, int pair_order, int ppw) {
   using C = DecodeCfg<D>;
   using Chunk = DecodeChunk<D, FP8>;
   using KVT = std::conditional_t<FP8, uint8_t, uint16_t>;
   using Piece = typename Chunk::Piece;
   __shared__ __attribute__((aligned(16))) char smem[NW * C::WAVE_LDS];
   __shared__ float sm_m[NW][16];
+  // split with several partitions per wave: the finished partitions' normalised partials wait in
+  // dynamic LDS until the wave has stopped streaming (a global store among loads in flight would
+  // make every later wait drain them all)
+  extern __shared__ __attribute__((aligned(16))) float stage[];
   __shared__ float sm_l[NW][16];
 
   const int p = blockIdx.x;
@@ -116,13 +121,19 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
   const int t_lo = window > 0 ? max(0, L - window) : 0;
   int t_begin = t_lo & ~31, t_end = L;
   if constexpr (SPLIT) {
-    t_begin = max(p * PT, t_begin);
-    t_end = min(L, p * PT + PT);
+    // partitions p*ppw .. p*ppw + ppw - 1, streamed by one wave
+    t_begin = max(p * ppw * PT, t_begin);
+    t_end = min(L, (p * ppw + ppw) * PT);
     if (t_begin >= t_end) return;  // uniform over the work-group (no partial is written)
   }
+  const int p_first = SPLIT ? t_begin / PT : 0;  // partition of the first chunk
+  int next_boundary = SPLIT ? (p_first + 1) * PT : 0;
 
   const int gcol = hg * 16 + col;
   const bool col_ok = gcol < G;
+  // staged partial slot: the group's valid head columns x (D + 4) floats, then m and l per column
+  const int n_valid = min(16, G - hg * 16);
+  const int slot_floats = n_valid * (D + 4) + 32;
   const int hq = kh * G + min(gcol, G - 1);
 
   // B operand of QK: q[hq][kk*32 + 8*qg .. +8]
@@ -259,6 +270,28 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
       o[mt] = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, o[mt]);
     }
     __builtin_amdgcn_wave_barrier();
+    if constexpr (SPLIT && NW == 1) {
+      if (cs + 32 == next_boundary && next_boundary < t_end) {
+        // a partition is complete: park its partial, start the next one afresh
+        const float lt = sum_xor32(sum_xor16(l_run));
+        const float inv = lt > 0.f ? v_scale / lt : 0.f;
+        float* sl = stage + (next_boundary / PT - 1 - p_first) * slot_floats;
+        if (col_ok) {
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt)
+            *reinterpret_cast<f32x4*>(sl + col * (D + 4) + mt * 16 + 4 * qg) = o[mt] * inv;
+          if (qg == 0) {
+            sl[n_valid * (D + 4) + col] = m_run;
+            sl[n_valid * (D + 4) + 16 + col] = lt;
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.f;
+        next_boundary += PT;
+      }
+    }
   };
 
   // chunks w, w+NW, ... with the next kPrefetch-1 chunks' loads in flight while one is processed.
@@ -298,13 +331,28 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
     const int hout = kh * G + gcol;
     const float inv = l_run > 0.f ? v_scale / l_run : 0.f;
     if constexpr (SPLIT) {
-      const size_t pi = ((size_t)b * Pmax + p) * Hq + hout;
+      const int p_last = (t_end - 1) / PT;
+      const size_t pi = ((size_t)b * Pmax + p_last) * Hq + hout;
       float* op = o_part + pi * D + 4 * qg;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) *reinterpret_cast<f32x4*>(op + mt * 16) = o[mt] * inv;
       if (qg == 0) {
         m_part[pi] = m_run;
         l_part[pi] = l_run;
+      }
+      // the parked partitions p_first .. p_last - 1
+      for (int pp = p_first; pp < p_last; ++pp) {
+        const float* sl = stage + (pp - p_first) * slot_floats;
+        const size_t pj = ((size_t)b * Pmax + pp) * Hq + hout;
+        float* fp = o_part + pj * D + 4 * qg;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+          *reinterpret_cast<f32x4*>(fp + mt * 16) =
+              *reinterpret_cast<const f32x4*>(sl + col * (D + 4) + mt * 16 + 4 * qg);
+        if (qg == 0) {
+          m_part[pj] = sl[n_valid * (D + 4) + col];
+          l_part[pj] = sl[n_valid * (D + 4) + 16 + col];
+        }
       }
     } else {
       uint16_t* op = out + ((size_t)b * Hq + hout) * D + 4 * qg;
@@ -358,17 +406,8 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
       acc[i] = a * inv;
     }
     const int hout = kh * G + hg * 16 + oc;
-    if constexpr (SPLIT) {
-      const size_t pi = ((size_t)b * Pmax + p) * Hq + hout;
-      float* op = o_part + pi * D + dpart * DPT;
-#pragma unroll
-      for (int i = 0; i < DPT; i += 4)
-        *reinterpret_cast<f32x4*>(op + i) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
-      if (dpart == 0) {
-        m_part[pi] = M;
-        l_part[pi] = lsum;
-      }
-    } else if (o_part != nullptr) {
+    static_assert(!SPLIT, "split partitions run single-wave work-groups");
+    if (o_part != nullptr) {
       // streamed attention: fold this launch's (max, exp-sum, normalised output) into the running
       // state of (b, hout). The column's threads are one wave: every lane reads before any writes.
       const size_t si = (size_t)b * Hq + hout;
@@ -548,13 +587,19 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   if (!(scale_log2 >= 1.17549435e-38f)) scale_log2 = 1.17549435e-38f;  // zero (or denormal) scale
   const int bs_shift = __builtin_ctz((unsigned)a.block_size);
   if (a.partition_tokens > 0) {
-    const dim3 grid(a.max_partitions, a.num_kv_heads * n_hg, a.batch);
-    hipLaunchKernelGGL((decode_kernel<D, 1, true, FP8>), grid, dim3(kWave), 0, stream,
+    // Long contexts: a wave streams up to 8 consecutive partitions (one start-up per stream; longer
+    // streams also keep the memory system busier), parking all but the last partial in LDS.
+    const int slot_bytes = (std::min(16, G) * (D + 4) + 32) * (int)sizeof(float);
+    int ppw = 1;
+    if (a.max_partitions >= 64) ppw = std::min(8, 1 + kMaxStageBytes / slot_bytes);
+    const size_t stage_bytes = (size_t)(ppw - 1) * slot_bytes;
+    const dim3 grid((a.max_partitions + ppw - 1) / ppw, a.num_kv_heads * n_hg, a.batch);
+    hipLaunchKernelGGL((decode_kernel<D, 1, true, FP8>), grid, dim3(kWave), stage_bytes, stream,
                        (const uint16_t*)a.q, (const KVT*)a.k_cache, (const KVT*)a.v_cache,
                        a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, a.o_part, a.m_part,
                        a.l_part, a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size,
                        a.num_blocks, a.max_blocks_per_seq, a.partition_tokens, a.max_partitions,
-                       scale_log2, v_scale, negate_q, bs_shift, a.window, 0);
+                       scale_log2, v_scale, negate_q, bs_shift, a.window, 0, ppw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // long splits take 1024 threads per (head, sequence), so one batch of loads covers them
@@ -578,7 +623,7 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
                      a.block_tables, a.seq_lens, (uint16_t*)a.out, a.lse, a.o_part, a.m_part,
                      a.l_part, a.num_q_heads, a.num_kv_heads, G, n_hg, a.block_size, a.num_blocks,
                      a.max_blocks_per_seq, 0, 1, scale_log2, v_scale, negate_q, bs_shift, a.window,
-                     (a.batch <= 64 && a.o_part == nullptr) ? 1 : 0);
+                     (a.batch <= 64 && a.o_part == nullptr) ? 1 : 0, 1);
   return hipGetLastError();
 }
 

@@ -53,6 +53,28 @@ EDGE = [
 ]
 
 
+# Long sequences (64 or more partitions): a wave streams several consecutive partitions and parks
+# the finished partials in LDS; lengths that end inside a wave's range and a partial head group
+LONG = [
+    # lens, Hq, Hkv, D, pt
+    ([33000 + 17, 40000], 4, 2, 64, 512),
+    ([70000, 512 * 64, 1], 40, 2, 128, 512),   # G = 20: the second head group has 4 columns
+    ([2048 * 64 + 5], 8, 4, 256, 2048),
+    ([64 * 64 + 31, 100], 2, 1, 128, 64),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LONG)))
+def test_decode_long_multi_partition(case):
+    lens, hq, hkv, d, pt = LONG[case]
+    di = paged_decode_inputs(1500 + case, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seq_lens=lens)
+    ref, rlse = oracle.paged_decode(di.q, di.k_cache, di.v_cache, di.block_tables, di.seq_lens, di.scale,
+                                    return_lse=True)
+    out, lse = _run(di, pt, with_lse=True)
+    print(f"long decode {LONG[case]}", assert_parity(out, ref, f"long decode {LONG[case]}"))
+    np.testing.assert_allclose(lse.double().numpy(), rlse, rtol=0, atol=2e-3)
+
+
 @pytest.mark.parametrize("case", range(len(EDGE)))
 @pytest.mark.parametrize("pt", [0, 64, 512])
 def test_decode_edge_shapes(case, pt):
