@@ -37,7 +37,7 @@ constexpr int kDirectWaves = 4;  // waves per work-group on the direct path (spl
 constexpr float kRescaleLog2 = 8.0f;  // raise a running max only when exceeded by more than this
 constexpr int kPrefetch = 2;          // 32-token chunks per wave in flight (loads issued ahead)
 constexpr int kMergeUnroll = 8;       // merge: partial rows per thread in flight
-constexpr int kMaxStageBytes = 32 * 1024;  // split: LDS for parked partials per wave
+constexpr int kMaxStageBytes = 68 * 1024;  // split: LDS for parked partials per wave
 
 template <int D>
 struct DecodeCfg {
@@ -587,11 +587,20 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   if (!(scale_log2 >= 1.17549435e-38f)) scale_log2 = 1.17549435e-38f;  // zero (or denormal) scale
   const int bs_shift = __builtin_ctz((unsigned)a.block_size);
   if (a.partition_tokens > 0) {
-    // Long contexts: a wave streams up to 8 consecutive partitions (one start-up per stream; longer
-    // streams also keep the memory system busier), parking all but the last partial in LDS.
+    // Long contexts: a wave streams up to 16 consecutive partitions (fewer, longer streams run
+    // faster), parking all but the last partial in LDS; the largest count that the LDS budget
+    // allows and that still leaves 512 waves (two per CU) is taken.
     const int slot_bytes = (std::min(16, G) * (D + 4) + 32) * (int)sizeof(float);
     int ppw = 1;
-    if (a.max_partitions >= 64) ppw = std::min(8, 1 + kMaxStageBytes / slot_bytes);
+    if (a.max_partitions >= 64) {
+      const long units = (long)a.batch * a.num_kv_heads * n_hg;
+      const int lds_cap = 1 + kMaxStageBytes / slot_bytes;
+      for (int c = 16; c > 1; c /= 2)
+        if (c <= lds_cap && units * ((a.max_partitions + c - 1) / c) >= 512) {
+          ppw = c;
+          break;
+        }
+    }
     const size_t stage_bytes = (size_t)(ppw - 1) * slot_bytes;
     const dim3 grid((a.max_partitions + ppw - 1) / ppw, a.num_kv_heads * n_hg, a.batch);
     hipLaunchKernelGGL((decode_kernel<D, 1, true, FP8>), grid, dim3(kWave), stage_bytes, stream,

@@ -53,14 +53,15 @@ EDGE = [
 ]
 
 
-# Long sequences (64 or more partitions): a wave streams several consecutive partitions and parks
-# the finished partials in LDS; lengths that end inside a wave's range and a partial head group
+# Long sequences (64 or more partitions) at batch x heads large enough that a wave streams several
+# consecutive partitions and parks the finished partials in LDS (the launch keeps at least 512
+# waves): partial head groups, head_dim 256, a count capped by the LDS budget, ragged ends
 LONG = [
     # lens, Hq, Hkv, D, pt
-    ([33000 + 17, 40000], 4, 2, 64, 512),
-    ([70000, 512 * 64, 1], 40, 2, 128, 512),   # G = 20: the second head group has 4 columns
-    ([2048 * 64 + 5], 8, 4, 256, 2048),
-    ([64 * 64 + 31, 100], 2, 1, 128, 64),
+    ([65536 + 17, 60000], 16, 2, 64, 32),       # G = 8: 16 partitions per wave
+    ([70000, 64 * 1000 + 1], 40, 2, 128, 64),   # G = 20: the second head group has 4 columns
+    ([70000 + 5, 3000], 8, 4, 256, 64),         # head_dim 256
+    ([20000, 19999], 32, 2, 256, 32),           # G = 16 at head_dim 256: 4 per wave (LDS cap)
 ]
 
 
