@@ -158,3 +158,19 @@ def test_split_and_direct_agree():
         assert_parity(x, ref, n)
     assert (a.float() - b.float()).abs().max() <= 2e-2
     assert (la - lb).abs().max() <= 2e-3 and (la - lc).abs().max() <= 2e-3
+
+
+@pytest.mark.parametrize("window", [40000, 2000])
+def test_decode_long_multi_partition_window(window):
+    """A sliding window over long sequences: with 40000 keys visible a wave streams several
+    partitions starting inside the window; with 2000 one partition per wave."""
+    di = paged_decode_inputs(1600, num_q_heads=16, num_kv_heads=2, head_dim=64, seq_lens=[65536 + 17, 60000])
+    ref, rlse = oracle.paged_decode_window(di.q, di.k_cache, di.v_cache, di.block_tables, di.seq_lens,
+                                           di.scale, window, return_lse=True)
+    q, kc, vc, bt, sl = _dev(di)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=DEV)
+    out = pkv.paged_attn_decode(q, kc, vc, bt, sl, di.scale, max_seq_len=di.max_seq_len, partition_tokens=32,
+                                lse=lse, window=window)
+    torch.cuda.synchronize()
+    print(f"long window decode {window}", assert_parity(out.cpu(), ref, f"long window decode {window}"))
+    np.testing.assert_allclose(lse.cpu().double().numpy(), rlse, rtol=0, atol=2e-3)
