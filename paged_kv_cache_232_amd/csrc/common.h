@@ -126,6 +126,41 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// Direct-to-LDS 16-byte load (gfx950 global_load_lds_dwordx4): lane i reads the 16 bytes at
+// base + voff_i and writes them to LDS bytes [lds + 16 i, lds + 16 i + 16), so one instruction
+// fills 1 KiB of LDS contiguously. base and lds are made wave-uniform (SGPR base, M0). The load is
+// written as asm so that the compiler's wait-count pass does not track it: it would otherwise wait
+// for every such load in flight before any LDS read, and a fence at a barrier waits for all of them
+// too. Callers wait with wait_vm_barrier() below. M0 is saved and restored around the load. The
+// instruction has no destination register, so nothing in registers is written behind the
+// compiler's back.
+__device__ __forceinline__ void dma_load16(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                     ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
+  const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(u), "s"(l)
+      : "memory");
+}
+
+// Waits until at most N of this wave's vector-memory loads (dma_load16 included) are still in
+// flight and all its LDS operations are done, then joins the work-group barrier. Vector loads
+// complete in issue order, so N counts the most recent loads that may stay outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // acc + the sum of 8 bf16 values (two per v_dot2_f32_bf16 against (1, 1); the products are exact)
 __device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
   const u32x4 u = __builtin_bit_cast(u32x4, p);

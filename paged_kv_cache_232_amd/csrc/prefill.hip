@@ -8,16 +8,21 @@
 //
 // MI355X design (a dense contraction, so MFMA-bound):
 //   * work-group = 4 waves; tile = 128 query rows of one q head (32 rows per wave);
-//   * K and V tiles of BN keys are staged row-major in LDS, loaded with 16-byte vector loads and
-//     prefetched into registers one tile ahead;
+//   * head_dim <= 128: K and V tiles of BN keys go straight from HBM into LDS with direct-to-LDS
+//     loads (global_load_lds_dwordx4), K two tiles ahead and V one tile ahead in rings of 3 and
+//     2 tiles, their 16-byte units permuted within each row so that the MFMA operand reads are
+//     free of bank conflicts; one explicit wait and barrier per tile;
+//   * head_dim 256 (16-row form below): tiles are loaded into registers two tiles ahead and
+//     staged into padded LDS rows (direct-to-LDS loads measured slower there);
+//   * the QK^T MFMAs are scheduled with four LDS reads of K in flight;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the wave's Q rows held in
 //     registers for the whole kernel), so each lane holds 16 keys of ONE query: the row max needs
 //     one cross-lane step, and the lane's probabilities are already the B operand of
 //     O^T += V^T P^T with no lane exchange;
 //   * softmax in the log2 domain; causal kv tiles above the diagonal are skipped, only tiles that
 //     cross the diagonal or the ragged end are masked;
-//   * q heads are mapped to block x so that the work-groups sharing one kv head land on one XCD
-//     (its L2 then serves the K/V re-reads of every q tile and every head of the group);
+//   * work-groups are mapped to XCDs so that all q heads sharing one kv head run on one XCD
+//     (its L2 then serves the K/V re-reads of every head of the group);
 //   * q tiles are issued last-first (the longest causal rows start first).
 #include <math.h>
 
@@ -45,6 +50,54 @@ constexpr int kBM = 32 * kPrefillWaves;  // query rows per work-group
 // A row's running max is only raised (and O, l rescaled) when a tile's max exceeds it by more than
 // this many log2 units; otherwise probabilities are taken against the stale max and stay <= 2^8.
 constexpr float kRescaleLog2 = 8.0f;
+// LDS reads of K kept in flight ahead of the QK^T MFMAs (4 measured best; 2 is the default schedule)
+constexpr int kQkAhead = 4;
+
+// Work-group (x, y) -> (q head h, schedule row y). The hardware deals work-groups to the 8 XCDs
+// round robin by linear id, i.e. by x % 8 when Hq % 8 == 0. With xcd_group = 8 / Hkv > 0, each
+// group of xcd_group consecutive y rows holds 8 G work-groups and XCD c takes the G q heads of
+// kv head c % Hkv for row y0 + c / Hkv: every q head that reads one K/V stream runs on one XCD,
+// whose L2 then serves the re-reads. Else, with xcd_heads = Hq / 8 > 0, XCD c takes q heads
+// c * xcd_heads .. +xcd_heads-1 of every row; else the plain mapping.
+__device__ __forceinline__ void xcd_map(int Hq, int Hkv, int G, int xcd_group, int xcd_heads,
+                                        int& h, int& y) {
+  h = blockIdx.x;
+  y = blockIdx.y;
+  if (xcd_group > 0) {
+    const int idg = (int)(blockIdx.y % xcd_group) * Hq + (int)blockIdx.x;
+    const int c = idg & 7;
+    h = (c % Hkv) * G + (idg >> 3);
+    y = (int)blockIdx.y - (int)(blockIdx.y % xcd_group) + c / Hkv;
+  } else if (xcd_heads > 0) {
+    h = (blockIdx.x & 7) * xcd_heads + (blockIdx.x >> 3);
+  }
+}
+
+// Scheduling hint for the QK^T loop of N MFMAs, each fed by one LDS read of K: keep AHEAD reads
+// in flight ahead of the MFMAs (the default schedule issues them two at a time, just before use,
+// so each MFMA pair waits out an LDS latency).
+template <int N, int AHEAD>
+__device__ __forceinline__ void sched_qk_pipeline() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+// One K or V tile of BN keys sits in LDS unpadded (row r at r * D elements) with its 16-byte units
+// permuted within the row: logical unit c of row r is stored at unit c ^ swz(r). A direct-to-LDS
+// load writes 1 KiB contiguously, so rows cannot be padded; the permutation instead spreads the
+// reads below over all 64 banks: 16 consecutive rows read at one logical unit (K as the MFMA A
+// operand, 16 lanes per LDS cycle) land on 16 different units, and 4 rows x 4 units of a V^T
+// transpose read (32 lanes per cycle) on 16 different units. It depends on r & 15 only.
+template <int UPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (UPR == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);  // 2 rows per 256 bytes
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
 
 template <int D>
 struct PrefillCfg {
@@ -53,21 +106,17 @@ struct PrefillCfg {
   static constexpr int MT = BN / 32;                // 32-key tiles of S^T
   static constexpr int PS = BN / 16;                // 16-key steps of PV
   static constexpr int DT = D / 32;                 // 32-wide d tiles of O^T
-  // LDS row strides in elements. K rows (read 16 bytes per lane, 8 rows per LDS cycle) take a
-  // 16-byte pad; V rows (transpose-read 8 bytes per lane, 4 rows x 64 bytes per 32 lanes) take a
-  // 64-byte pad, which spreads those rows over all 64 banks. Both measured conflict-free.
-  static constexpr int RSE = D + 8;                 // K rows and the output tile
-  static constexpr int RSV = D + 32;                // V rows
-  static constexpr int BUF = BN * (RSE + RSV);      // one K+V tile buffer
   static constexpr int UPR = D / 8;                 // 16-byte units per row
-  static constexpr int UNITS = BN * UPR;            // units per tile (K or V)
-  static constexpr int UPT = UNITS / kPrefillThreads;  // units per thread
-  // kv tiles held in registers between their loads and their LDS stage: the loads of tile t+PF+1
-  // are issued while tile t is consumed (one tile of compute does not cover a load's latency).
-  static constexpr int PF = (D >= 128) ? 2 : 1;
-  // two K+V tile buffers (double buffering), later reused for the output tile
-  static constexpr int LDS_ELEMS = (2 * BUF > kBM * RSE) ? 2 * BUF : kBM * RSE;
-  static_assert(UNITS % kPrefillThreads == 0, "tile units must divide evenly");
+  static constexpr int TILE = BN * D;               // elements of one K or V tile
+  static constexpr int ROWS_PER_LOAD = kWave / UPR; // rows one wave load instruction fills
+  static constexpr int NL = BN * UPR / (kWave * kPrefillWaves);  // load instructions per wave per tile
+  static constexpr int RSO = D + 8;                 // row stride of the staged output tile
+  // K tiles in a ring of 3 (loaded two tiles ahead), V tiles in a ring of 2 (one tile ahead)
+  static constexpr int KBUF = 3, VBUF = 2;
+  static constexpr int LDS_ELEMS =
+      ((KBUF + VBUF) * TILE > kBM * RSO) ? (KBUF + VBUF) * TILE : kBM * RSO;
+  static_assert(NL * kWave * kPrefillWaves == BN * UPR, "tile units must divide evenly");
+  static_assert(ROWS_PER_LOAD <= 16, "a load instruction's rows must stay inside one block");
 };
 
 struct RaggedLoader {
@@ -98,23 +147,24 @@ struct PagedLoader {
 // scale_log2 > 0 always: the host folds a negative scale into negate_q (an exact sign flip of q)
 // and replaces a zero scale by the smallest normal float (every score then rounds to 2^0 = 1).
 template <int D, bool PAGED>
-__global__ void __launch_bounds__(kPrefillThreads, D <= 128 ? 2 : 1)
+__global__ void __launch_bounds__(kPrefillThreads, 2)
 prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
                const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
                const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ tables,
                int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
-               int negate_q, int xcd_heads, int bs_shift, const TileOrder order) {
+               int negate_q, int xcd_group, int xcd_heads, int n_rows, int bs_shift,
+               const TileOrder order) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
-  // buffer j (0/1): K rows at smem + j*BUF, V rows BN*RSE further
+  // K ring at smem + j * TILE (j < 3), V ring after it; the output tile reuses the space
 
-  // block x -> q head: heads sharing a kv head go to the same XCD (round-robin x % 8)
-  int h = blockIdx.x;
-  if (xcd_heads > 0) h = (blockIdx.x & 7) * xcd_heads + (blockIdx.x >> 3);
-  const uint32_t sched = order.n > 0 ? order.e[min((int)blockIdx.y, kMaxOrder - 1)] : 0u;
-  const int b = order.n > 0 ? (int)(sched >> 16) : (int)blockIdx.y;
   const int G = Hq / Hkv;
+  int h, y;
+  xcd_map(Hq, Hkv, G, xcd_group, xcd_heads, h, y);
+  if (y >= n_rows) return;
+  const uint32_t sched = order.n > 0 ? order.e[min(y, kMaxOrder - 1)] : 0u;
+  const int b = order.n > 0 ? (int)(sched >> 16) : y;
   const int kh = h / G;
 
   const int q0 = qo_indptr[b];
@@ -173,80 +223,74 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   const RaggedLoader rl{kv0, Hkv, kh, D};
   const PagedLoader pl{tables + (size_t)b * max_blocks, Hkv, kh, D, BS, NB, bs_shift};
-  static_assert(kWave * 16 / (2 * D) <= 16, "a wave's load rows must stay inside one block");
 
-  u32x4 kpre[C::PF][C::UPT], vpre[C::PF][C::UPT];
-  const int w_u0 = __builtin_amdgcn_readfirstlane(tid & ~63);  // first unit of this wave
-  // Loads of tile rows n0 .. n0+BN-1; rows past the request's end re-read its last row (their
-  // probabilities are exactly 0). Every call issues the same loads in the same order, whatever
-  // n0 is, so the wait before each stage counts exactly the loads still needed.
-  const int last_n0 = (n_kt - 1) * C::BN;  // first row of the last tile
-  auto fetch = [&](int n0, auto slot_c) {
-    constexpr int sl = decltype(slot_c)::value;
-    n0 = __builtin_amdgcn_readfirstlane(min(n0, last_n0));  // past the last tile: repeat it
+  // Loads of one K or V tile (rows n0 .. n0+BN-1) straight into LDS: load instruction i of wave w
+  // fills 1 KiB chunk j = i * waves + w of the tile, lane l its physical unit 64 j + l, i.e. row
+  // rr = (64 j + l) / UPR, stored unit l % UPR, which holds logical unit (l % UPR) ^ swz(rr).
+  // Rows past the request's end re-read its last row (their probabilities are exactly 0).
+  const uint32_t lds0 = lds_addr(smem);
+  const int pc = lane % C::UPR;
+  auto load_tile = [&](const uint16_t* src, int t, uint32_t lds_tile) {
+    const int n0 = t * C::BN;
     const int last_r = kv - 1 - n0;  // >= 0: the tile's last row inside the request
 #pragma unroll
-    for (int i = 0; i < C::UPT; ++i) {
-      const int u = i * kPrefillThreads + tid;
-      const int rr = u / C::UPR;
-      const int cu = u - rr * C::UPR;
+    for (int i = 0; i < C::NL; ++i) {
+      const int j = i * kPrefillWaves + w;                 // wave-uniform
+      const int rr = j * C::ROWS_PER_LOAD + lane / C::UPR;
+      const int cu = pc ^ swz<C::UPR>(rr);
       const int r = min(rr, last_r);
-      size_t base;  // wave-uniform element offset
-      int off;      // per-lane byte offset
+      size_t base;   // wave-uniform element offset
+      uint32_t vo;   // per-lane byte offset
       if constexpr (PAGED) {
         // the instruction's first row: wave-uniform, in the same block as every row it loads
-        const int nb = min(n0 + (i * kPrefillThreads + w_u0) / C::UPR, kv - 1);
+        const int nb = min(n0 + j * C::ROWS_PER_LOAD, kv - 1);
         base = pl.block_offset(nb);
-        off = (__umul24((n0 + r) & (BS - 1), D) + cu * 8) * 2;  // 24-bit products (host-checked)
+        vo = (uint32_t)(__umul24((n0 + r) & (BS - 1), D) + cu * 8) * 2u;
       } else {
         base = rl.row_offset(n0);
-        off = (__umul24(r, Hkv * D) + cu * 8) * 2;
+        vo = (uint32_t)(__umul24(r, Hkv * D) + cu * 8) * 2u;  // 24-bit products (host-checked)
       }
-      kpre[sl][i] = buffer_load16(buffer_at(k + base), off);
-      vpre[sl][i] = buffer_load16(buffer_at(v + base), off);
-      memory_order_point();
+      dma_load16(src + base, vo, lds_tile + (uint32_t)j * 1024u);
     }
   };
-  auto stash = [&](int buf, auto slot_c) {
-    constexpr int sl = decltype(slot_c)::value;
-    uint16_t* const k_lds = smem + buf * C::BUF;
-    uint16_t* const v_lds = k_lds + C::BN * C::RSE;
-#pragma unroll
-    for (int i = 0; i < C::UPT; ++i) {
-      const int u = i * kPrefillThreads + tid;
-      const int rr = u / C::UPR;
-      const int cu = u - rr * C::UPR;
-      *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[sl][i];
-      *reinterpret_cast<u32x4*>(v_lds + rr * C::RSV + cu * 8) = vpre[sl][i];
-    }
-  };
+  auto k_lds_of = [&](int slot) { return lds0 + (uint32_t)(slot * C::TILE * 2); };
+  auto v_lds_of = [&](int slot) { return lds0 + (uint32_t)((C::KBUF + slot) * C::TILE * 2); };
 
-  // Transpose-read addresses of the V^T operand: 16-lane group g reads key rows
-  // 4*(g/2) + (l%16)/4 (+8 for the second read) at columns 16*(g%2) + 4*(l%4) of each d tile.
+  // LDS read offsets (elements, within a tile). K as the A operand: row mt*32 + qcol, logical
+  // unit 2 ks + half. V^T transpose reads: 16-lane group g reads key rows 4*(g/2) + (l%16)/4
+  // (+8 for the second read) at columns 16*(g%2) + 4*(l%4) of each 32-wide d tile, i.e. logical
+  // unit 4 dt + cq, element 4*(l%2) within it.
+  const int swk = swz<C::UPR>(qcol);
   const int grp = lane >> 4;
   const int tr_row = 4 * (grp >> 1) + ((lane & 15) >> 2);
-  const int tr_col = 16 * (grp & 1) + 4 * (lane & 3);
+  const int cq = 2 * (grp & 1) + ((lane & 3) >> 1);
+  const int sw_lo = swz<C::UPR>(tr_row), sw_hi = swz<C::UPR>(tr_row + 8);
+  const int tr_lo = tr_row * D + 4 * (lane & 1);
+  const int tr_hi = (tr_row + 8) * D + 4 * (lane & 1);
 
-  // Double-buffered LDS tiles: tile t+1 is staged into the other buffer while tile t is consumed,
-  // with the loads of tiles t+2 .. t+PF+1 already in flight; one barrier per tile. Register slot
-  // (tile % PF) holds a tile from its loads to its stage.
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, (C::PF > 1) ? 1 : 0>;
+  // Pipeline, per wave: issue order K0 V0 K1 | V1 K2 | V2 K3 | ... (step t issues V(t+1) and
+  // K(t+2)); so before step t only K(t+1)'s NL loads may still be in flight.
   if (n_kt > 0) {
-    fetch(0, S0{});
-    stash(0, S0{});
-    fetch(C::BN, S1{});
-    if constexpr (C::PF > 1) fetch(2 * C::BN, S0{});
+    load_tile(k, 0, k_lds_of(0));
+    load_tile(v, 0, v_lds_of(0));
+    if (n_kt > 1) load_tile(k, 1, k_lds_of(1));
   }
   // last key any row of this wave can see (causal): tiles past it are skipped by the wave
   const int wave_last_key = causal ? m0 + w * 32 + 31 + off : 0x7fffffff;
-  // one kv tile; slot_c is the register slot of tile t+1
-  auto step = [&](int t, auto slot_c) {
+  int ks_slot = 0;  // t % 3
+  for (int t = 0; t < n_kt; ++t) {
     const int n0 = t * C::BN;
-    __syncthreads();  // tile t staged by every wave; tile t-1's buffer no longer read
-    const uint16_t* const k_lds = smem + (t & 1) * C::BUF;
-    const uint16_t* const v_lds = k_lds + C::BN * C::RSE;
-    if (n0 <= wave_last_key) {
+    // tile t landed for every wave; every wave is done with tile t-1's buffers
+    if (t + 1 < n_kt) wait_vm_barrier<C::NL>();
+    else wait_vm_barrier<0>();
+    const int ks_next2 = ks_slot >= 1 ? ks_slot - 1 : 2;  // (t + 2) % 3
+    if (t + 1 < n_kt) load_tile(v, t + 1, v_lds_of((t + 1) & 1));
+    if (t + 2 < n_kt) load_tile(k, t + 2, k_lds_of(ks_next2));
+    const uint16_t* const k_lds = smem + ks_slot * C::TILE;
+    const uint16_t* const v_lds = smem + (C::KBUF + (t & 1)) * C::TILE;
+    ks_slot = ks_slot == 2 ? 0 : ks_slot + 1;
+    if (n0 > wave_last_key) continue;
+
     // S^T tile: lane holds keys n0 + mt*32 + 8*(r/4) + 4*half + r%4 of query qcol (raw scores)
     f32x16 s[C::MT];
 #pragma unroll
@@ -258,9 +302,10 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            k_lds + (mt * 32 + qcol) * C::RSE + ks * 16 + 8 * half));
+            k_lds + (mt * 32 + qcol) * D + (((2 * ks + half) ^ swk) << 3)));
         s[mt] = mfma32(a, qreg[ks], s[mt]);
       }
+    sched_qk_pipeline<C::KS * C::MT, kQkAhead>();
 
     // mask only tiles crossing the ragged end or this wave's causal diagonal
     const bool need_mask = (n0 + C::BN > kv) || (causal && n0 + C::BN - 1 > m0 + w * 32 + off);
@@ -309,44 +354,24 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int st = 0; st < C::PS; ++st)
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const uint16_t* vp = v_lds + (16 * st + tr_row) * C::RSV + dt * 32 + tr_col;
-        const u32x2 lo = lds_read_tr16(vp);
-        const u32x2 hi = lds_read_tr16(vp + 8 * C::RSV);
+        const uint16_t* vt = v_lds + st * 16 * D;
+        const u32x2 lo = lds_read_tr16(vt + tr_lo + (((4 * dt + cq) ^ sw_lo) << 3));
+        const u32x2 hi = lds_read_tr16(vt + tr_hi + (((4 * dt + cq) ^ sw_hi) << 3));
         o[dt] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[st], o[dt]);
       }
-    }
-    // Unconditional, also after the last tile (a stage nobody reads, loads of clamped rows), so
-    // every path into the next step has issued the same loads.
-    stash((t + 1) & 1, slot_c);
-    fetch(n0 + (1 + C::PF) * C::BN, slot_c);
-  };
-  if (n_kt > 0) {
-    if constexpr (C::PF == 1) {
-      int t = 0;
-      do {
-        step(t, S0{});
-      } while (++t < n_kt);
-    } else {
-      for (int t = 0;; t += 2) {
-        step(t, S1{});
-        if (t + 1 >= n_kt) break;
-        step(t + 1, S0{});
-        if (t + 2 >= n_kt) break;
-      }
-    }
   }
 
   // normalise, stage the wave's 32 rows in LDS, then write whole rows with 16-byte stores
   l_run = sum_xor32(l_run);
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  __syncthreads();
-  uint16_t* const ost = smem + w * 32 * C::RSE;
+  __syncthreads();  // no tile loads in flight (the last step waited for all), no tile reads left
+  uint16_t* const ost = smem + w * 32 * C::RSO;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = dt * 32 + 8 * g + 4 * half;
-      *reinterpret_cast<u32x2*>(ost + qcol * C::RSE + d) =
+      *reinterpret_cast<u32x2*>(ost + qcol * C::RSO + d) =
           u32x2{pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
                 pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
     }
@@ -358,10 +383,9 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int orow = m0 + w * 32 + rr;
     if (orow < qo)
       store16(out + ((size_t)(q0 + orow) * Hq + h) * D + cu * 8,
-              *reinterpret_cast<const u32x4*>(ost + rr * C::RSE + cu * 8));
+              *reinterpret_cast<const u32x4*>(ost + rr * C::RSO + cu * 8));
   }
 }
-
 // ------------------------------------------------------------------------------------------------
 // Variant with 16 query rows per wave on v_mfma_f32_16x16x32_bf16: 8 waves x 16 rows = the same
 // 128-row q tile, but each wave holds half the output accumulator and half the q rows, so two
@@ -406,16 +430,18 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
                  const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ tables,
                  int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
-                 int negate_q, int xcd_heads, int bs_shift, const TileOrder order) {
+                 int negate_q, int xcd_group, int xcd_heads, int n_rows, int bs_shift,
+               const TileOrder order) {
   using C = P16Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
   // buffer j (0/1): K rows at smem + j*BUF, V rows BN*RSE further; the output tile reuses it
 
-  int h = blockIdx.x;
-  if (xcd_heads > 0) h = (blockIdx.x & 7) * xcd_heads + (blockIdx.x >> 3);
-  const uint32_t sched = order.n > 0 ? order.e[min((int)blockIdx.y, kMaxOrder - 1)] : 0u;
-  const int b = order.n > 0 ? (int)(sched >> 16) : (int)blockIdx.y;
   const int G = Hq / Hkv;
+  int h, y;
+  xcd_map(Hq, Hkv, G, xcd_group, xcd_heads, h, y);
+  if (y >= n_rows) return;
+  const uint32_t sched = order.n > 0 ? order.e[min(y, kMaxOrder - 1)] : 0u;
+  const int b = order.n > 0 ? (int)(sched >> 16) : y;
   const int kh = h / G;
 
   const int q0 = qo_indptr[b];
@@ -548,6 +574,7 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               k_lds + (kt * 16 + qcol) * C::RSE + ks * 32 + 8 * grp));
           s[kt] = mfma16(a, qreg[ks], s[kt]);
         }
+      sched_qk_pipeline<C::KS * C::KT, kQkAhead>();
       const bool need_mask =
           (n0 + C::BN > kv) || (causal && n0 + C::BN - 1 > wave_first_row + off);
       if (need_mask) {
@@ -688,25 +715,31 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
   if (n_qt == 0) return hipSuccess;
   TileOrder order;
   build_order(a, order);
-  const int xcd_heads = (a.num_q_heads % 8 == 0) ? a.num_q_heads / 8 : 0;
+  const bool q8 = a.num_q_heads % 8 == 0;
+  const int xcd_group = (q8 && 8 % a.num_kv_heads == 0) ? 8 / a.num_kv_heads : 0;
+  const int xcd_heads = (q8 && xcd_group == 0) ? a.num_q_heads / 8 : 0;
+  const int n_rows = order.n > 0 ? order.n : a.batch;
+  const int grid_rows = xcd_group > 0 ? (n_rows + xcd_group - 1) / xcd_group * xcd_group : n_rows;
   float scale_log2 = a.scale * kLog2e;
   const int negate_q = scale_log2 < 0.f;
   if (negate_q) scale_log2 = -scale_log2;
   if (!(scale_log2 >= 1.17549435e-38f)) scale_log2 = 1.17549435e-38f;  // zero (or denormal) scale
-  const dim3 grid = order.n > 0 ? dim3(a.num_q_heads, order.n, 1) : dim3(a.num_q_heads, a.batch, n_qt);
+  const dim3 grid = order.n > 0 ? dim3(a.num_q_heads, grid_rows, 1) : dim3(a.num_q_heads, grid_rows, n_qt);
   const int bs_shift = a.block_size > 0 ? __builtin_ctz((unsigned)a.block_size) : 0;
   if constexpr (use_p16<D>()) {
     hipLaunchKernelGGL((prefill16_kernel<D, PAGED>), grid, dim3(kP16Threads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
                        a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
-                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads, bs_shift, order);
+                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_group, xcd_heads, n_rows, bs_shift,
+                       order);
   } else {
     hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(kPrefillThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
                        a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
-                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_heads, bs_shift, order);
+                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_group, xcd_heads, n_rows, bs_shift,
+                       order);
   }
   return hipGetLastError();
 }
