@@ -34,6 +34,14 @@ RAGGED_EDGE = [
     ([700, 31], [1500, 31], 2, 2, 64, True),        # long prefix offset, head_dim 64
     ([600, 90], [600, 4000], 4, 2, 128, False),     # non-causal, kv much longer than q
     ([1] * 800, [37] * 800, 2, 1, 64, True),         # more q tiles than the launch schedule holds
+    # XCD placement of work-groups: heads of one kv head grouped on an XCD over 8 / Hkv schedule
+    # rows (row counts not a multiple of the group pad the grid), the per-XCD head mapping when
+    # Hkv does not divide 8, and the plain grid
+    ([130, 70, 260], None, 16, 16, 128, True),      # Hkv = 16: per-XCD heads
+    ([200, 17], None, 24, 3, 64, True),             # Hkv = 3: per-XCD heads, head_dim 64
+    ([129, 5, 300], None, 8, 1, 128, True),         # group of 8 rows, 6 rows used
+    ([129, 40, 1], [129, 90, 1], 16, 4, 256, True), # group of 2 rows, 4 rows, head_dim 256
+    ([1] * 801, [37] * 801, 8, 2, 128, True),       # plain grid (801 requests), group of 4
 ]
 
 
@@ -73,6 +81,9 @@ PAGED_EDGE = [
     ([50, 129], [16, 100], 4, 1, 128, 32),
     ([33], [5000], 2, 2, 64, 64),
     ([600, 257], [700, 0], 4, 2, 128, 16),
+    ([9, 200, 129], [300, 0, 2000], 16, 4, 256, 16),  # 5 schedule rows in groups of 2
+    ([77, 1, 256], [33, 4000, 16], 8, 1, 64, 16),     # groups of 8, head_dim 64
+    ([140, 60], [900, 45], 32, 8, 128, 32),           # one row per group
 ]
 
 
