@@ -52,16 +52,16 @@ METRIC = "decode KV GB/s (% HBM peak); ragged-prefill bf16 TFLOP/s (% MFMA peak)
 # mismatch reports traffic as null.
 CSRC = os.path.join(ROOT, "paged_kv_cache_232_amd", "csrc")
 TRAFFIC = {
-    "scatter5": (("cache.hip",), "af79fc58ea7b66d4", 71274709),
-    "paged5": (("prefill.hip", "common.h"), "6ed5458691ad06dc", 549630634),
-    "ragged2": (("prefill.hip", "common.h"), "6ed5458691ad06dc", 206203221),
-    "decode3": (("decode.hip", "common.h"), "0dadec0f277b1c5f", 1019689173),
-    "decode3_direct": (("decode.hip", "common.h"), "0dadec0f277b1c5f", 1019658634),
-    "decode3_split": (("decode.hip", "common.h"), "0dadec0f277b1c5f", 1039416341),
-    "decode4": (("decode.hip", "common.h"), "0dadec0f277b1c5f", 2220563114),
-    "decode3_fp8": (("decode.hip", "common.h"), "0dadec0f277b1c5f", 510975104),
-    "decode4_fp8": (("decode.hip", "common.h"), "0dadec0f277b1c5f", 1147640378),
-    "copy_blocks": (("blocks.hip",), "f683f208ca662bf5", 1073885265),
+    "scatter5": (("cache.hip",), "af79fc58ea7b66d4", 71274368),
+    "paged5": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 547439104),
+    "ragged2": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 194861653),
+    "decode3": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1019398528),
+    "decode3_direct": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1019389818),
+    "decode3_split": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1039562675),
+    "decode4": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 2220556021),
+    "decode3_fp8": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 510789109),
+    "decode4_fp8": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1147497035),
+    "copy_blocks": (("blocks.hip",), "f683f208ca662bf5", 1073887467),
 }
 
 

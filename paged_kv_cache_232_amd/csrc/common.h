@@ -111,6 +111,13 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Non-temporal 16-byte store (global_store ... nt): for outputs no later kernel of the same pass
+// re-reads soon. Prefill output written this way streams to HBM while the (compute-bound) kernel
+// runs, instead of lingering dirty in the caches and being written back during the next kernel.
+__device__ __forceinline__ void store16_nt(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 // Raw buffer resource over memory starting at a wave-uniform address (no bounds limit: callers
 // keep every offset inside their tensors). Loads through it take a 32-bit per-lane byte offset,
 // so a tile's addresses cost one VALU op per unit instead of a 64-bit add per load.

@@ -63,6 +63,17 @@ __device__ __forceinline__ u32x4 piece_bf16(u32x4 x) { return x; }
 __device__ __forceinline__ u32x4 piece_bf16(u32x2 x) { return fp8x8_to_bf16x8(x); }
 __device__ __forceinline__ u32x4 load_piece(const uint16_t* p, u32x4*) { return load16(p); }
 __device__ __forceinline__ u32x2 load_piece(const uint8_t* p, u32x2*) { return load8(p); }
+// V pieces are read with the non-temporal policy: each V load instruction reads whole 128-byte
+// lines (a contiguous 1 KiB, or 512 bytes of fp8 codes, per wave) that nothing reads again, and
+// keeping them out of the caches' normal replacement measured 8-15 % faster on every bf16 and
+// fp8 decode workload. K loads keep the default policy: each instruction reads part of a line
+// whose rest the next instructions read, and non-temporal K loads measured slower.
+__device__ __forceinline__ u32x4 load_piece_nt(const uint16_t* p, u32x4*) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 load_piece_nt(const uint8_t* p, u32x2*) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
 
 
 // scale_log2 > 0 always: the host folds a negative scale into negate_q (an exact sign flip of q)
@@ -187,7 +198,7 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk) ch.k[hh][kk] = load_piece(kp + koff + kk * 32, (Piece*)nullptr);
 #pragma unroll
-      for (int i = 0; i < C::VU; ++i) ch.v[hh][i] = load_piece(vp + voff + i * 512, (Piece*)nullptr);
+      for (int i = 0; i < C::VU; ++i) ch.v[hh][i] = load_piece_nt(vp + voff + i * 512, (Piece*)nullptr);
     }
   };
 

@@ -382,7 +382,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int cu = u - rr * C::UPR;
     const int orow = m0 + w * 32 + rr;
     if (orow < qo)
-      store16(out + ((size_t)(q0 + orow) * Hq + h) * D + cu * 8,
+      store16_nt(out + ((size_t)(q0 + orow) * Hq + h) * D + cu * 8,
               *reinterpret_cast<const u32x4*>(ost + rr * C::RSO + cu * 8));
   }
 }
@@ -667,7 +667,7 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int cu = u - rr * C::UPR;
     const int orow = wave_first_row + rr;
     if (orow < qo)
-      store16(out + ((size_t)(q0 + orow) * Hq + h) * D + cu * 8,
+      store16_nt(out + ((size_t)(q0 + orow) * Hq + h) * D + cu * 8,
               *reinterpret_cast<const u32x4*>(ost + rr * C::RSE + cu * 8));
   }
 }

@@ -77,7 +77,7 @@ def test_decode_long_multi_partition(case):
 
 
 @pytest.mark.parametrize("case", range(len(EDGE)))
-@pytest.mark.parametrize("pt", [0, 64, 512])
+@pytest.mark.parametrize("pt", [0, 64, 512, 1024])
 def test_decode_edge_shapes(case, pt):
     lens, hq, hkv, d, bs = EDGE[case]
     di = paged_decode_inputs(1000 + case, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seq_lens=lens,
@@ -97,7 +97,7 @@ def config3():
     return di, _dev(di)
 
 
-@pytest.mark.parametrize("pt", [0, 512])
+@pytest.mark.parametrize("pt", [0, 512, 2048])
 def test_batched_decode_config_full(config3, pt):
     di, dev = config3
     ref = oracle.paged_decode(di.q, di.k_cache, di.v_cache, di.block_tables, di.seq_lens, di.scale)
@@ -160,17 +160,19 @@ def test_split_and_direct_agree():
     assert (la - lb).abs().max() <= 2e-3 and (la - lc).abs().max() <= 2e-3
 
 
+@pytest.mark.parametrize("pt", [32, 1024])
 @pytest.mark.parametrize("window", [40000, 2000])
-def test_decode_long_multi_partition_window(window):
-    """A sliding window over long sequences: with 40000 keys visible a wave streams several
-    partitions starting inside the window; with 2000 one partition per wave."""
+def test_decode_long_multi_partition_window(window, pt):
+    """A sliding window over long sequences: with 32-token partitions and 40000 keys visible a wave
+    streams several partitions starting inside the window, with 2000 one partition per wave; with
+    1024-token partitions a partition's first chunk may start inside the window."""
     di = paged_decode_inputs(1600, num_q_heads=16, num_kv_heads=2, head_dim=64, seq_lens=[65536 + 17, 60000])
     ref, rlse = oracle.paged_decode_window(di.q, di.k_cache, di.v_cache, di.block_tables, di.seq_lens,
                                            di.scale, window, return_lse=True)
     q, kc, vc, bt, sl = _dev(di)
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=DEV)
-    out = pkv.paged_attn_decode(q, kc, vc, bt, sl, di.scale, max_seq_len=di.max_seq_len, partition_tokens=32,
+    out = pkv.paged_attn_decode(q, kc, vc, bt, sl, di.scale, max_seq_len=di.max_seq_len, partition_tokens=pt,
                                 lse=lse, window=window)
     torch.cuda.synchronize()
-    print(f"long window decode {window}", assert_parity(out.cpu(), ref, f"long window decode {window}"))
+    print(f"long window decode {window} pt={pt}", assert_parity(out.cpu(), ref, f"long window decode {window} pt={pt}"))
     np.testing.assert_allclose(lse.cpu().double().numpy(), rlse, rtol=0, atol=2e-3)

@@ -75,7 +75,7 @@ FP8_SHAPES = [
 
 
 @pytest.mark.parametrize("case", range(len(FP8_SHAPES)))
-@pytest.mark.parametrize("pt", [0, 512])
+@pytest.mark.parametrize("pt", [0, 512, 1024])
 def test_fp8_decode_shapes(case, pt):
     lens, hq, hkv, d, bs = FP8_SHAPES[case]
     di = paged_decode_inputs(3000 + case, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seq_lens=lens,
