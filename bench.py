@@ -52,16 +52,16 @@ METRIC = "decode KV GB/s (% HBM peak); ragged-prefill bf16 TFLOP/s (% MFMA peak)
 # mismatch reports traffic as null.
 CSRC = os.path.join(ROOT, "paged_kv_cache_232_amd", "csrc")
 TRAFFIC = {
-    "scatter5": (("cache.hip",), "af79fc58ea7b66d4", 71274368),
-    "paged5": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 547439104),
-    "ragged2": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 194861653),
-    "decode3": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1019398528),
-    "decode3_direct": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1019389818),
-    "decode3_split": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1039562675),
-    "decode4": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 2220556021),
-    "decode3_fp8": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 510789109),
-    "decode4_fp8": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1147497035),
-    "copy_blocks": (("blocks.hip",), "f683f208ca662bf5", 1073887467),
+    "scatter5": (("cache.hip",), "af79fc58ea7b66d4", 71275349),
+    "paged5": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 547370538),
+    "ragged2": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 194826453),
+    "decode3": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1019428864),
+    "decode3_direct": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1019396510),
+    "decode3_split": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1039573226),
+    "decode4": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 2220548608),
+    "decode3_fp8": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 510811688),
+    "decode4_fp8": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1147480736),
+    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073911654),
 }
 
 
