@@ -11,23 +11,39 @@
 
 namespace pkv {
 
+template <bool POW2>
 __global__ void __launch_bounds__(256)
 reshape_and_cache_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
                          u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
                          const int64_t* __restrict__ slot_mapping, int64_t num_units,
                          int units_per_token, int units_per_row, int block_size,
-                         int64_t num_slots) {
+                         int64_t num_slots, int upt_shift, int upr_shift, int bs_shift) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int heads = units_per_token / units_per_row;
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < num_units; u += stride) {
-    const int64_t t = u / units_per_token;
+    // POW2: units per token, units per row and block size are powers of two (shifts and masks
+    // instead of 64-bit divisions, which the GPU emulates with dozens of instructions)
+    int64_t t, blk, off;
+    int h, c;
+    if constexpr (POW2) {
+      t = u >> upt_shift;
+    } else {
+      t = u / units_per_token;
+    }
     const int r = (int)(u - t * units_per_token);  // unit within the token: head * units_per_row + c
     const int64_t slot = slot_mapping[t];
     if (slot < 0 || slot >= num_slots) continue;
-    const int h = r / units_per_row;
-    const int c = r - h * units_per_row;
-    const int64_t blk = slot / block_size;
-    const int64_t off = slot - blk * block_size;
-    const int heads = units_per_token / units_per_row;
+    if constexpr (POW2) {
+      h = r >> upr_shift;
+      c = r & (units_per_row - 1);
+      blk = slot >> bs_shift;
+      off = slot & (block_size - 1);
+    } else {
+      h = r / units_per_row;
+      c = r - h * units_per_row;
+      blk = slot / block_size;
+      off = slot - blk * block_size;
+    }
     const int64_t dst = ((blk * heads + h) * block_size + off) * units_per_row + c;
     const u32x4 kv = k[u];
     const u32x4 vv = v[u];
@@ -35,6 +51,8 @@ reshape_and_cache_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ 
     v_cache[dst] = vv;
   }
 }
+
+static bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
@@ -47,10 +65,18 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
   const int threads = 256;
   int64_t blocks = (num_units + threads - 1) / threads;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                     (const u32x4*)k, (const u32x4*)v, (u32x4*)k_cache, (u32x4*)v_cache,
-                     slot_mapping, num_units, units_per_token, units_per_row, block_size,
-                     (int64_t)num_blocks * block_size);
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  if (is_pow2(units_per_token) && is_pow2(units_per_row) && is_pow2(block_size))
+    hipLaunchKernelGGL((reshape_and_cache_kernel<true>), dim3((unsigned)blocks), dim3(threads), 0,
+                       stream, (const u32x4*)k, (const u32x4*)v, (u32x4*)k_cache, (u32x4*)v_cache,
+                       slot_mapping, num_units, units_per_token, units_per_row, block_size,
+                       num_slots, __builtin_ctz((unsigned)units_per_token),
+                       __builtin_ctz((unsigned)units_per_row), __builtin_ctz((unsigned)block_size));
+  else
+    hipLaunchKernelGGL((reshape_and_cache_kernel<false>), dim3((unsigned)blocks), dim3(threads), 0,
+                       stream, (const u32x4*)k, (const u32x4*)v, (u32x4*)k_cache, (u32x4*)v_cache,
+                       slot_mapping, num_units, units_per_token, units_per_row, block_size,
+                       num_slots, 0, 0, 0);
   return hipGetLastError();
 }
 

@@ -37,6 +37,17 @@ def test_scatter_shapes_and_skipped_slots(hq, hkv, d, bs):
     _scatter_and_compare(ci, slots)
 
 
+@pytest.mark.parametrize("hkv,d,bs", [(3, 128, 16), (2, 72, 16), (1, 64, 12)])
+def test_scatter_shapes_not_powers_of_two(hkv, d, bs):
+    """Units per token, units per row or block size not a power of two: the division path."""
+    ci = chunked_prefill_inputs(500 + d + bs, num_q_heads=hkv, num_kv_heads=hkv, head_dim=d, chunk_lens=[1, 37, 16],
+                                prefix_lens=[5, 0, 16], block_size=bs, num_blocks=None)
+    _scatter_and_compare(ci)
+    slots = ci.slot_mapping.clone()
+    slots[1::4] = -1
+    _scatter_and_compare(ci, slots)
+
+
 def test_scatter_zero_tokens_is_noop():
     ci = chunked_prefill_inputs(9, num_q_heads=2, num_kv_heads=1, head_dim=64, chunk_lens=[3], prefix_lens=[0])
     kc = ci.k_cache.to(DEV)
