@@ -52,16 +52,16 @@ METRIC = "decode KV GB/s (% HBM peak); ragged-prefill bf16 TFLOP/s (% MFMA peak)
 # mismatch reports traffic as null.
 CSRC = os.path.join(ROOT, "paged_kv_cache_232_amd", "csrc")
 TRAFFIC = {
-    "scatter5": (("cache.hip",), "ca92b19357222b29", 71237418),
-    "paged5": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 547230336),
-    "ragged2": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 195075498),
-    "decode3": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1019436373),
-    "decode3_direct": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1019401195),
-    "decode3_split": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1039572238),
-    "decode4": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 2220539850),
-    "decode3_fp8": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 510807813),
-    "decode4_fp8": (("decode.hip", "common.h"), "f8bd9c66d43e8b2f", 1147472928),
-    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073903636),
+    "scatter5": (("cache.hip",), "ca92b19357222b29", 71237717),
+    "paged5": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 547315968),
+    "ragged2": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 194928554),
+    "decode3": (("decode.hip", "common.h"), "b06982d139bdfd1c", 1019142528),
+    "decode3_direct": (("decode.hip", "common.h"), "b06982d139bdfd1c", 1019131340),
+    "decode3_split": (("decode.hip", "common.h"), "b06982d139bdfd1c", 1039543457),
+    "decode4": (("decode.hip", "common.h"), "b06982d139bdfd1c", 2220503946),
+    "decode3_fp8": (("decode.hip", "common.h"), "b06982d139bdfd1c", 510806896),
+    "decode4_fp8": (("decode.hip", "common.h"), "b06982d139bdfd1c", 1147494236),
+    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073901537),
 }
 
 

@@ -10,8 +10,10 @@
 //     of <= 16 q heads) with the next chunk's loads already in flight while one is processed;
 //     split-KV: one single-wave work-group per partition; direct: 4 waves per sequence take
 //     chunks round robin and are combined through LDS at the end;
-//   * QK^T on a 16x16x32 bf16 MFMA with the K half page as the A operand (rows = 16 tokens, loaded
-//     straight from HBM in 16-byte pieces) and the GQA group's q rows as B (16 columns);
+//   * QK^T on a 16x16x32 bf16 MFMA with the K half page as the A operand (rows = 16 tokens) and
+//     the GQA group's q rows as B (16 columns); a bf16 K half page is read in contiguous 1 KiB
+//     wave loads and staged through the wave's LDS tile (which V then reuses), an fp8 one is
+//     loaded straight into the operand layout in 8-byte pieces;
 //   * the score tile lands in the layout the PV MFMA needs for its B operand: each lane already
 //     holds 8 probabilities of one head, so P never moves between lanes;
 //   * V is read from HBM in contiguous 1 KiB wave loads, staged row-major in a per-wave LDS tile
@@ -45,6 +47,7 @@ struct DecodeCfg {
   static constexpr int MT = D / 16;           // 16-row d tiles of the PV MFMA
   static constexpr int VU = D / 32;           // 16-byte V units per lane per half page
   static constexpr int RS = 2 * D + 32;       // LDS bytes per staged V row (pad: conflict-free tr reads)
+  static constexpr int RSK = 2 * D + 16;      // LDS bytes per staged K row (pad: conflict-free reads)
   static constexpr int WAVE_LDS = 32 * RS;    // one wave's 32-row V tile
   static_assert(WAVE_LDS >= D * 16 * 4, "combine buffer must fit in a wave's V tile");
 };
@@ -63,11 +66,12 @@ __device__ __forceinline__ u32x4 piece_bf16(u32x4 x) { return x; }
 __device__ __forceinline__ u32x4 piece_bf16(u32x2 x) { return fp8x8_to_bf16x8(x); }
 __device__ __forceinline__ u32x4 load_piece(const uint16_t* p, u32x4*) { return load16(p); }
 __device__ __forceinline__ u32x2 load_piece(const uint8_t* p, u32x2*) { return load8(p); }
-// V pieces are read with the non-temporal policy: each V load instruction reads whole 128-byte
-// lines (a contiguous 1 KiB, or 512 bytes of fp8 codes, per wave) that nothing reads again, and
-// keeping them out of the caches' normal replacement measured 8-15 % faster on every bf16 and
-// fp8 decode workload. K loads keep the default policy: each instruction reads part of a line
-// whose rest the next instructions read, and non-temporal K loads measured slower.
+// Non-temporal loads for pieces whose load instruction reads whole 128-byte lines that nothing
+// reads again: V always (a contiguous 1 KiB, or 512 bytes of fp8 codes, per wave), and K of a
+// bf16 cache, which is read the same way and staged through LDS. Keeping these lines out of the
+// caches' normal replacement measured 8-15 % faster on the decode workloads. fp8 K is loaded
+// straight in the MFMA operand layout, where an instruction reads only part of each line (the
+// next instructions read the rest); it keeps the default policy, which measured faster there.
 __device__ __forceinline__ u32x4 load_piece_nt(const uint16_t* p, u32x4*) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -196,7 +200,11 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
       const KVT* kp = kc + base;
       const KVT* vp = vc + base;
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) ch.k[hh][kk] = load_piece(kp + koff + kk * 32, (Piece*)nullptr);
+      for (int i = 0; i < C::KK; ++i) {
+        // bf16: whole 1 KiB rows like V (staged through LDS below); fp8: the MFMA operand pieces
+        if constexpr (FP8) ch.k[hh][i] = load_piece(kp + koff + i * 32, (Piece*)nullptr);
+        else ch.k[hh][i] = load_piece_nt(kp + voff + i * 512, (Piece*)nullptr);
+      }
 #pragma unroll
       for (int i = 0; i < C::VU; ++i) ch.v[hh][i] = load_piece_nt(vp + voff + i * 512, (Piece*)nullptr);
     }
@@ -208,12 +216,36 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
     const bool partial = cs + 31 > last || cs < t_lo;
     // S^T[token][head] for the two half pages
     f32x4 s[2];
+    if constexpr (FP8) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int hh = 0; hh < 2; ++hh) {
+        s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk)
-        s[hh] = mfma16(as_bf16x8(piece_bf16(ch.k[hh][kk])), qreg[kk], s[hh]);
+        for (int kk = 0; kk < C::KK; ++kk)
+          s[hh] = mfma16(as_bf16x8(piece_bf16(ch.k[hh][kk])), qreg[kk], s[hh]);
+      }
+    } else {
+      // K rows staged in the wave's LDS tile (row stride RSK), read back as the A operand; the V
+      // rows then overwrite the tile (LDS operations of one wave run in order)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < C::KK; ++i) {
+          const int u = i * 64 + lane;
+          const int row = u / (D / 8);
+          *reinterpret_cast<u32x4*>(vbuf + (16 * hh + row) * C::RSK + (u - row * (D / 8)) * 16) = ch.k[hh][i];
+        }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk)
+          s[hh] = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(
+                             vbuf + (16 * hh + col) * C::RSK + (32 * kk + 8 * qg) * 2)),
+                         qreg[kk], s[hh]);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
     // stage V rows in LDS; rows past the end are zeroed (select, so NaN slack never leaks)
     if (!partial) {
