@@ -52,16 +52,16 @@ METRIC = "decode KV GB/s (% HBM peak); ragged-prefill bf16 TFLOP/s (% MFMA peak)
 # mismatch reports traffic as null.
 CSRC = os.path.join(ROOT, "paged_kv_cache_232_amd", "csrc")
 TRAFFIC = {
-    "scatter5": (("cache.hip",), "ca92b19357222b29", 71237717),
-    "paged5": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 547315968),
-    "ragged2": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 194928554),
-    "decode3": (("decode.hip", "common.h"), "b06982d139bdfd1c", 1019142528),
-    "decode3_direct": (("decode.hip", "common.h"), "b06982d139bdfd1c", 1019131340),
-    "decode3_split": (("decode.hip", "common.h"), "b06982d139bdfd1c", 1039543457),
-    "decode4": (("decode.hip", "common.h"), "b06982d139bdfd1c", 2220503946),
-    "decode3_fp8": (("decode.hip", "common.h"), "b06982d139bdfd1c", 510806896),
-    "decode4_fp8": (("decode.hip", "common.h"), "b06982d139bdfd1c", 1147494236),
-    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073901537),
+    "scatter5": (("cache.hip",), "ca92b19357222b29", 71237162),
+    "paged5": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 547509376),
+    "ragged2": (("prefill.hip", "common.h"), "9f2ec510ca9c32c2", 195046229),
+    "decode3": (("decode.hip", "common.h"), "129d7b34160e5974", 1019155029),
+    "decode3_direct": (("decode.hip", "common.h"), "129d7b34160e5974", 1019117706),
+    "decode3_split": (("decode.hip", "common.h"), "129d7b34160e5974", 1039545315),
+    "decode4": (("decode.hip", "common.h"), "129d7b34160e5974", 2220510368),
+    "decode3_fp8": (("decode.hip", "common.h"), "129d7b34160e5974", 510796252),
+    "decode4_fp8": (("decode.hip", "common.h"), "129d7b34160e5974", 1146872783),
+    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073893150),
 }
 
 

@@ -635,14 +635,14 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     // allows and that still leaves 512 waves (two per CU) is taken.
     const int slot_bytes = (std::min(16, G) * (D + 4) + 32) * (int)sizeof(float);
     // Partitions holding visible keys: with a sliding window only the last ones. The fp8 cache
-    // keeps one partition per wave (measured faster there).
+    // streams at most two partitions per wave (measured fastest there: four or more were slower).
     int p_act = a.max_partitions;
     if (a.window > 0) p_act = std::min(p_act, (a.window + 31) / a.partition_tokens + 2);
     int ppw = 1;
-    if (!FP8 && p_act >= 64) {
+    if (p_act >= 64) {
       const long units = (long)a.batch * a.num_kv_heads * n_hg;
       const int lds_cap = 1 + kMaxStageBytes / slot_bytes;
-      for (int c = 16; c > 1; c /= 2)
+      for (int c = FP8 ? 2 : 16; c > 1; c /= 2)
         if (c <= lds_cap && units * ((p_act + c - 1) / c) >= 512) {
           ppw = c;
           break;

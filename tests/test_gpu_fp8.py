@@ -106,6 +106,16 @@ def test_fp8_long_context_split_decode():
     print("fp8 long split decode", assert_parity(out, ref, "fp8 long split decode"))
 
 
+def test_fp8_long_multi_partition_streamed():
+    """fp8 cache over 500+ 32-token partitions: a wave streams two consecutive partitions and parks
+    the first one's partial in LDS."""
+    di = paged_decode_inputs(3250, num_q_heads=16, num_kv_heads=8, head_dim=128, seq_lens=[16384 + 17, 12000])
+    kq, vq = _fp8_inputs(di, 0.05, 0.05)
+    ref = oracle.paged_decode_fp8(di.q, kq, vq, di.block_tables, di.seq_lens, di.scale, 0.05, 0.05)
+    out, _ = _decode_fp8(di, kq, vq, 0.05, 0.05, 32)
+    print("fp8 long streamed decode", assert_parity(out, ref, "fp8 long streamed decode"))
+
+
 def test_fp8_gpu_scatter_then_decode_equals_oracle():
     # new tokens quantised by the GPU scatter, then decoded: the caches equal the oracle's (the
     # scatter is bit-exact), so the decode matches the oracle over the oracle's own caches
