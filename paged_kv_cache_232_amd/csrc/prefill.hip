@@ -230,9 +230,32 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // Rows past the request's end re-read its last row (their probabilities are exactly 0).
   const uint32_t lds0 = lds_addr(smem);
   const int pc = lane % C::UPR;
+  // Per-lane byte offsets of a whole tile (no row past the request's end), the same for K and V
+  // and for every such tile: computed once. (Paged: rows n0 + r sit at offset r & (BS-1) of their
+  // block when BS divides the tile's first row, i.e. BS <= BN.)
+  uint32_t vo_full[C::NL];
+#pragma unroll
+  for (int i = 0; i < C::NL; ++i) {
+    const int rr = (i * kPrefillWaves + w) * C::ROWS_PER_LOAD + lane / C::UPR;
+    const int cu = pc ^ swz<C::UPR>(rr);
+    if constexpr (PAGED) vo_full[i] = (uint32_t)(__umul24(rr & (BS - 1), D) + cu * 8) * 2u;
+    else vo_full[i] = (uint32_t)(__umul24(rr, Hkv * D) + cu * 8) * 2u;
+  }
+  const bool bs_in_tile = !PAGED || BS <= C::BN;
   auto load_tile = [&](const uint16_t* src, int t, uint32_t lds_tile) {
     const int n0 = t * C::BN;
     const int last_r = kv - 1 - n0;  // >= 0: the tile's last row inside the request
+    if (bs_in_tile && n0 + C::BN <= kv) {
+#pragma unroll
+      for (int i = 0; i < C::NL; ++i) {
+        const int j = i * kPrefillWaves + w;  // wave-uniform
+        size_t base;
+        if constexpr (PAGED) base = pl.block_offset(n0 + j * C::ROWS_PER_LOAD);
+        else base = rl.row_offset(n0);
+        dma_load16(src + base, vo_full[i], lds_tile + (uint32_t)j * 1024u);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < C::NL; ++i) {
       const int j = i * kPrefillWaves + w;                 // wave-uniform
