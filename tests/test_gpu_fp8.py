@@ -139,3 +139,53 @@ def test_fp8_gpu_scatter_then_decode_equals_oracle():
                                 partition_tokens=0, k_scale=k_scale, v_scale=v_scale)
     torch.cuda.synchronize()
     print("fp8 scatter+decode", assert_parity(out.cpu(), ref, "fp8 scatter then decode"))
+
+
+def _fp8_workload_sampled(cid, pt, checks, seed):
+    """A whole decode workload over fp8 caches at the timed launch (scales 0.02, as timed). The
+    checked (sequence, kv head) slices hold the oracle's codes of the workload's cache, every other
+    slice random finite codes; each checked slice is recomputed by the oracle on its own."""
+    di = make_config(cid)
+    k_scale = v_scale = 0.02
+    g = torch.Generator().manual_seed(seed)
+    kc = torch.randint(0, 0x7F, tuple(di.k_cache.shape), generator=g, dtype=torch.uint8)
+    vc = torch.randint(0, 0x7F, tuple(di.v_cache.shape), generator=g, dtype=torch.uint8)
+    bs = di.block_size
+    Hq, Hkv = di.q.shape[1], di.k_cache.shape[1]
+    G = Hq // Hkv
+    slices = []
+    for b, kh in checks:
+        L = int(di.seq_lens[b])
+        blocks = di.block_tables[b, :(L + bs - 1) // bs].long()
+        kq = oracle.quantize(di.k_cache[blocks, kh], k_scale)
+        vq = oracle.quantize(di.v_cache[blocks, kh], v_scale)
+        kc[blocks, kh] = torch.from_numpy(kq)
+        vc[blocks, kh] = torch.from_numpy(vq)
+        slices.append((b, kh, L, kq, vq))
+    out = pkv.paged_attn_decode(di.q.to(DEV), kc.to(DEV), vc.to(DEV), di.block_tables.to(DEV),
+                                di.seq_lens.to(DEV), di.scale, max_seq_len=di.max_seq_len,
+                                partition_tokens=pt, k_scale=k_scale, v_scale=v_scale)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    assert torch.isfinite(out.float()).all()
+    for b, kh, L, kq, vq in slices:
+        nblk = kq.shape[0]
+        ref = oracle.paged_decode_fp8(di.q[b:b + 1, kh * G:(kh + 1) * G], kq[:, None], vq[:, None],
+                                      torch.arange(nblk, dtype=torch.int32)[None], torch.tensor([L], dtype=torch.int32),
+                                      di.scale, k_scale, v_scale)
+        got = out[b:b + 1, kh * G:(kh + 1) * G]
+        print(f"fp8 workload {cid} (b={b}, kv head {kh})", assert_parity(got, ref, f"fp8 workload {cid} b={b} kh={kh}"))
+
+
+def test_fp8_batched_decode_workload_sampled():
+    """The batched decode workload (64 sequences, 512-8192 tokens) over fp8 caches, library's path."""
+    di = make_config(3)
+    longest = int(torch.argmax(di.seq_lens))
+    shortest = int(torch.argmin(di.seq_lens))
+    del di
+    _fp8_workload_sampled(3, -1, [(longest, 0), (shortest, 7), (17, 3), (40, 5)], 33)
+
+
+def test_fp8_long_context_decode_workload_sampled():
+    """The long-context workload (4 x 131072 tokens, 64 q / 8 kv heads) over fp8 caches, split 512."""
+    _fp8_workload_sampled(4, 512, [(0, 0), (3, 7)], 44)
