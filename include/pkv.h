@@ -14,9 +14,10 @@
  *     first ceil(len / block_size) entries of a row are read.
  *   - Query head h reads kv head h / (num_q_heads / num_kv_heads) (consecutive q heads share).
  *   - Return value: PKV_OK, or an error code; on error nothing was enqueued. Device-side
- *     preconditions (table contents, lengths, slots) are trusted for speed; the kernels clamp
- *     every address they form to the buffers described by the size arguments, so a broken table
- *     gives wrong numbers, never an out-of-bounds access. pkv_validate_block_tables_h checks them.
+ *     preconditions (table contents, lengths, offsets, slots) are trusted for speed; the kernels
+ *     clamp every address they form to the buffers described by the size arguments (and, for
+ *     prefill, by the host copies of the offsets), so a broken table or length gives wrong
+ *     numbers, never an out-of-bounds access. pkv_validate_block_tables_h checks tables.
  *   - Slots that hold no token (the tail of a sequence's last block, unused blocks) may hold any
  *     bits, NaN included: they are excluded by length, never read into a result.
  *
@@ -124,15 +125,36 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
  *   q, out   [qo_indptr_h[batch], num_q_heads, head_dim] bf16.
  *   k, v     [kv_indptr_h[batch], num_kv_heads, head_dim] bf16.
  *   qo_indptr, kv_indptr        device [batch + 1] int32 prefix sums (read by the kernel).
- *   qo_indptr_h, kv_indptr_h    host copies of the same (sizes the launch; no device sync).
- * PKV_E_UNSUPPORTED for head_dim other than 64/128/256 or num_kv_heads * head_dim >= 2^23 (also
- * for pkv_paged_prefill).
+ *   qo_indptr_h, kv_indptr_h    host copies of the same (size and order the launch; no device
+ *                               sync). The kernels clamp the device offsets to the buffers the
+ *                               host copies describe (q / out rows qo_indptr_h[batch], k / v rows
+ *                               kv_indptr_h[batch]): device offsets that disagree with their host
+ *                               copies give wrong rows, never an access outside those buffers.
+ *   workspace    device scratch of at least pkv_prefill_workspace_bytes(...) bytes (may be NULL
+ *                when that is 0), 16-byte aligned; it holds the work-group schedule the library
+ *                builds on the device. Its contents need no initialisation. Calls that share a
+ *                workspace must be ordered (one stream).
+ * The work of a launch is cut into (request, 128-row q tile) items run longest-first.
+ * PKV_E_UNSUPPORTED for head_dim other than 64/128/256, num_kv_heads * head_dim >= 2^23, batch >
+ * 65535, a request of more than 65535 q tiles, or more than 65528 q tiles in all (also for
+ * pkv_paged_prefill). PKV_E_WORKSPACE_TOO_SMALL when workspace_bytes is below the size above.
  */
 int pkv_ragged_prefill(const void* q, const void* k, const void* v, void* out,
                        const int32_t* qo_indptr, const int32_t* kv_indptr,
                        const int32_t* qo_indptr_h, const int32_t* kv_indptr_h, int32_t batch,
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t causal,
-                       float scale, void* stream);
+                       float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes pkv_ragged_prefill / pkv_paged_prefill need for these host q offsets
+ * (qo_indptr_h, [batch + 1]): 0 when the launch's longest-first schedule fits the launch
+ * arguments (at most 768 (request, q tile) items), else room for one 32-bit entry per item. The
+ * Atlas spark_runtime/flashinfer.rs page sizes its ragged-prefill workspaces the same way, from
+ * the batch's offsets before the call (atlas_fi_ragged_prefill_workspace_sizes). Returns 0 for
+ * arguments the prefill calls would reject.
+ */
+size_t pkv_prefill_workspace_bytes(int32_t batch, const int32_t* qo_indptr_h, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim);
 
 /*
  * paged_prefill — prefill whose keys/values come through the block table (chunked prefill over a
@@ -143,15 +165,18 @@ int pkv_ragged_prefill(const void* q, const void* k, const void* v, void* out,
  * when causal != 0.
  *
  *   q, out       [qo_indptr_h[batch], num_q_heads, head_dim] bf16.
- *   block_tables [batch, max_blocks_per_seq] int32; kv_lens device [batch] int32.
- *   qo_indptr    device [batch + 1]; qo_indptr_h, kv_lens_h host copies.
+ *   block_tables [batch, max_blocks_per_seq] int32; kv_lens device [batch] int32 (clamped to
+ *                max_blocks_per_seq * block_size by the kernels).
+ *   qo_indptr    device [batch + 1]; qo_indptr_h, kv_lens_h host copies (a host length beyond
+ *                the table's capacity is PKV_E_BAD_TABLE).
+ *   workspace, workspace_bytes   as for pkv_ragged_prefill (pkv_prefill_workspace_bytes).
  */
 int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* qo_indptr, const int32_t* kv_lens,
                       const int32_t* qo_indptr_h, const int32_t* kv_lens_h, void* out, int32_t batch,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                       int32_t num_blocks, int32_t max_blocks_per_seq, int32_t causal, float scale,
-                      void* stream);
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Checked-mode validation of block tables on the host, following the libmir-cuda page

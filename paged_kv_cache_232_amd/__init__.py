@@ -39,10 +39,11 @@ _SIGNATURES = {
                                              _c_i32, _c_f32, _c_i32, _c_ptr, _c_size, _c_ptr]),
     "pkv_ragged_prefill": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                           _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
-                                          _c_ptr]),
+                                          _c_ptr, _c_size, _c_ptr]),
+    "pkv_prefill_workspace_bytes": (_c_size, [_c_i32, _c_ptr, _c_i32, _c_i32, _c_i32]),
     "pkv_paged_prefill": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                          _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
-                                         _c_i32, _c_i32, _c_i32, _c_f32, _c_ptr]),
+                                         _c_i32, _c_i32, _c_i32, _c_f32, _c_ptr, _c_size, _c_ptr]),
     "pkv_validate_block_tables_h": (ctypes.c_int, [_c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pkv_reshape_and_cache_fp8": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32,
                                                  _c_i32, _c_i32, _c_i32, _c_f32, _c_f32, _c_ptr]),
@@ -122,6 +123,24 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
         raise ValueError(f"{name} must be a device tensor")
 
 
+def _need_out(t: torch.Tensor, name: str, dtype, shape, device):
+    """A caller-supplied output: dtype, shape, contiguity and device must match what the call writes."""
+    _need(t, name, dtype, len(shape), device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_workspace(ws: Optional[torch.Tensor], need: int, device) -> Optional[torch.Tensor]:
+    """A caller-supplied workspace (device bytes, contiguous, large enough), or a new one."""
+    if ws is None:
+        return torch.empty(need, dtype=torch.uint8, device=device) if need else None
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor on the call's device")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, the call needs {need}")
+    return ws
+
+
 def _host_i32(x) -> torch.Tensor:
     if isinstance(x, torch.Tensor):
         return x.detach().to("cpu", torch.int32).contiguous()
@@ -183,12 +202,11 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     if out is None:
         out = torch.empty_like(q)
     else:
-        _need(out, "out", torch.bfloat16, 3, dev)
+        _need_out(out, "out", torch.bfloat16, (B, Hq, D), dev)
     if lse is not None:
-        _need(lse, "lse", torch.float32, 2, dev)
+        _need_out(lse, "lse", torch.float32, (B, Hq), dev)
     need = decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len, partition_tokens) if B else 0
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _need_workspace(workspace, need, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if window:
         if fp8:
@@ -249,12 +267,20 @@ def decode_plan(seq_lens_h, num_q_heads: int, num_kv_heads: int, head_dim: int,
     return mx.value, pt.value, ws.value
 
 
+def prefill_workspace_bytes(qo_indptr_h, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
+    """Workspace bytes ragged_prefill / paged_prefill need for these host q offsets [B+1]."""
+    qh = _host_i32(qo_indptr_h)
+    return int(load_library().pkv_prefill_workspace_bytes(qh.numel() - 1, ctypes.c_void_p(qh.data_ptr()),
+                                                           num_q_heads, num_kv_heads, head_dim))
+
+
 def ragged_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qo_indptr: torch.Tensor,
                    kv_indptr: torch.Tensor, causal: bool, scale: float, *,
                    qo_indptr_h: Optional[Sequence[int]] = None, kv_indptr_h: Optional[Sequence[int]] = None,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Ragged (varlen) prefill. q [Tq, Hq, D], k/v [Tkv, Hkv, D], indptrs [B+1] int32 on the device.
-    Host copies of the indptrs size the launch; when omitted they are copied back (a device sync)."""
+    Host copies of the indptrs size the launch; when omitted they are copied back (a device sync).
+    ``workspace``: device bytes of at least prefill_workspace_bytes(...) (allocated when omitted)."""
     lib = load_library()
     dev = q.device
     _need(q, "q", torch.bfloat16, 3, dev)
@@ -274,10 +300,14 @@ def ragged_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qo_indptr:
     if out is None:
         out = torch.empty_like(q)
     else:
-        _need(out, "out", torch.bfloat16, 3, dev)
+        _need_out(out, "out", torch.bfloat16, (Tq, Hq, D), dev)
+    need = int(lib.pkv_prefill_workspace_bytes(B, ctypes.c_void_p(qh.data_ptr()), Hq, Hkv, D)) if B > 0 else 0
+    workspace = _need_workspace(workspace, need, dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pkv_ragged_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(qo_indptr), _ptr(kv_indptr),
                                   ctypes.c_void_p(qh.data_ptr()), ctypes.c_void_p(kh.data_ptr()), B, Hq,
-                                  Hkv, D, int(bool(causal)), float(scale), _stream(q)), "ragged_prefill")
+                                  Hkv, D, int(bool(causal)), float(scale), _ptr(workspace), wbytes, _stream(q)),
+           "ragged_prefill")
     return out
 
 
@@ -285,9 +315,10 @@ def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                   block_tables: torch.Tensor, qo_indptr: torch.Tensor, kv_lens: torch.Tensor,
                   causal: bool, scale: float, *, qo_indptr_h: Optional[Sequence[int]] = None,
                   kv_lens_h: Optional[Sequence[int]] = None,
-                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Prefill over a paged cache. q [Tq, Hq, D], caches [NB, Hkv, BS, D], block_tables [B, max_blocks]
-    int32, qo_indptr [B+1] and kv_lens [B] int32 on the device (host copies size the launch)."""
+    int32, qo_indptr [B+1] and kv_lens [B] int32 on the device (host copies size the launch).
+    ``workspace`` as for ragged_prefill."""
     lib = load_library()
     dev = q.device
     _need(q, "q", torch.bfloat16, 3, dev)
@@ -308,11 +339,15 @@ def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if out is None:
         out = torch.empty_like(q)
     else:
-        _need(out, "out", torch.bfloat16, 3, dev)
+        _need_out(out, "out", torch.bfloat16, (Tq, Hq, D), dev)
+    need = int(lib.pkv_prefill_workspace_bytes(B, ctypes.c_void_p(qh.data_ptr()), Hq, Hkv, D)) if B > 0 else 0
+    workspace = _need_workspace(workspace, need, dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pkv_paged_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(qo_indptr),
                                  _ptr(kv_lens), ctypes.c_void_p(qh.data_ptr()), ctypes.c_void_p(kh.data_ptr()),
                                  _ptr(out), B, Hq, Hkv, D, BS, NB, block_tables.shape[1],
-                                 int(bool(causal)), float(scale), _stream(q)), "paged_prefill")
+                                 int(bool(causal)), float(scale), _ptr(workspace), wbytes, _stream(q)),
+           "paged_prefill")
     return out
 
 
@@ -408,6 +443,8 @@ class StreamedDecode:
         NB, Hkv, BS, _ = self.k_cache.shape
         _need(tile_tables, "tile_tables", torch.int32, 2, self.q.device)
         _need(tile_lens, "tile_lens", torch.int32, 1, self.q.device)
+        if tile_tables.shape[0] != B or tile_lens.shape[0] != B:
+            raise ValueError("tile_tables / tile_lens must have one row per sequence")
         _check(load_library().pkv_stream_attn_step(_ptr(self.q), _ptr(self.k_cache), _ptr(self.v_cache),
                                                    _ptr(tile_tables), _ptr(tile_lens), _ptr(self.state),
                                                    self.nbytes, B, Hq, Hkv, D, BS, NB, tile_tables.shape[1],
@@ -415,7 +452,12 @@ class StreamedDecode:
 
     def finalize(self, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
         B, Hq, D = self.q.shape
-        out = torch.empty_like(self.q) if out is None else out
+        if out is None:
+            out = torch.empty_like(self.q)
+        else:
+            _need_out(out, "out", torch.bfloat16, (B, Hq, D), self.q.device)
+        if lse is not None:
+            _need_out(lse, "lse", torch.float32, (B, Hq), self.q.device)
         _check(load_library().pkv_stream_attn_finalize(_ptr(self.state), self.nbytes, _ptr(out), _ptr(lse),
                                                        B, Hq, D, _stream(self.q)), "stream_attn_finalize")
         return out

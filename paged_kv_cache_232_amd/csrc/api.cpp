@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "../../include/pkv.h"
+#include "api_internal.h"
 #include "kernels.h"
 
 namespace {
@@ -16,6 +17,10 @@ bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 bool block_size_ok(int bs) { return bs >= 16 && bs <= 256 && (bs & (bs - 1)) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_E_HIP; }
+
+// Prefill: q rows per work-group tile, and the most tiles one launch takes (one grid row each)
+constexpr int kPrefillTileRows = 128;
+constexpr int64_t kMaxPrefillGridRows = 65528;
 
 // Auto choice of the decode path. A direct launch gives one work-group per (sequence, kv head,
 // q-head group); when that is too few to fill 256 CUs several times over and sequences are
@@ -96,13 +101,13 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
 
 }  // extern "C"
 
-static int decode_impl(const void* q, const void* k_cache, const void* v_cache,
-                       const int32_t* block_tables, const int32_t* seq_lens, void* out, float* lse,
-                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                       int32_t max_seq_len, float scale, int32_t partition_tokens, void* workspace,
-                       size_t workspace_bytes, int kv_fp8, float k_scale, float v_scale,
-                       int window, void* stream) {
+int pkv::decode_checked(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* seq_lens, void* out, float* lse,
+                        int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                        int32_t max_seq_len, float scale, int32_t partition_tokens, void* workspace,
+                        size_t workspace_bytes, int kv_fp8, float k_scale, float v_scale,
+                        int window, void* stream) {
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_seq_len < 0 || partition_tokens < -1)
     return PKV_E_INVALID_ARGUMENT;
@@ -166,7 +171,7 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                           int32_t max_seq_len, float scale, int32_t partition_tokens, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
+  return pkv::decode_checked(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                      max_seq_len, scale, partition_tokens, workspace, workspace_bytes, 0, 1.f, 1.f,
                      0, stream);
@@ -180,7 +185,7 @@ int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_
                               float k_scale, float v_scale, int32_t partition_tokens,
                               void* workspace, size_t workspace_bytes, void* stream) {
   if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_E_INVALID_ARGUMENT;
-  return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
+  return pkv::decode_checked(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                      max_seq_len, scale, partition_tokens, workspace, workspace_bytes, 1, k_scale,
                      v_scale, 0, stream);
@@ -195,7 +200,7 @@ int pkv_paged_attn_decode_window(const void* q, const void* k_cache, const void*
                                  int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                                  void* stream) {
   if (window < 0) return PKV_E_INVALID_ARGUMENT;
-  return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
+  return pkv::decode_checked(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                      max_seq_len, scale, partition_tokens, workspace, workspace_bytes, 0, 1.f, 1.f,
                      window, stream);
@@ -299,19 +304,22 @@ int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void*
                                                       (hipStream_t)stream));
 }
 
+// Checks shared by both prefill forms, on the host copies of the q offsets: sizes, supported
+// shapes, and the schedule's limits (request and q-tile indices travel in 16 bits each, one grid
+// row per q tile).
 static int check_prefill_common(const void* q, const void* out, const int32_t* qo_indptr,
                                 const int32_t* qo_indptr_h, int32_t batch, int32_t num_q_heads,
-                                int32_t num_kv_heads, int32_t head_dim, int* max_qo, int* total_q) {
+                                int32_t num_kv_heads, int32_t head_dim, int* max_qo, int* total_q,
+                                int64_t* tiles) {
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0) return PKV_E_INVALID_ARGUMENT;
   if (num_q_heads % num_kv_heads != 0) return PKV_E_INVALID_ARGUMENT;
   if (!head_dim_ok(head_dim)) return PKV_E_UNSUPPORTED;
   // the kernels form a tile's per-lane K/V offsets with 24-bit multiplies of the row stride
   if ((int64_t)num_kv_heads * head_dim >= (1 << 23)) return PKV_E_UNSUPPORTED;
-  if (batch == 0) {
-    *max_qo = 0;
-    *total_q = 0;
-    return PKV_OK;
-  }
+  *max_qo = 0;
+  *total_q = 0;
+  *tiles = 0;
+  if (batch == 0) return PKV_OK;
   if (!qo_indptr_h || !qo_indptr) return PKV_E_INVALID_ARGUMENT;
   if (qo_indptr_h[0] != 0) return PKV_E_INVALID_ARGUMENT;
   int mx = 0;
@@ -324,18 +332,41 @@ static int check_prefill_common(const void* q, const void* out, const int32_t* q
   *total_q = qo_indptr_h[batch];
   if (*total_q > 0 && (!q || !out)) return PKV_E_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(out)) return PKV_E_INVALID_ARGUMENT;
-  if (batch > 65535) return PKV_E_UNSUPPORTED;
+  if (batch > 65535 || mx > 0xffff * kPrefillTileRows) return PKV_E_UNSUPPORTED;
+  *tiles = pkv::prefill_tile_count(batch, qo_indptr_h);
+  if (*tiles > kMaxPrefillGridRows) return PKV_E_UNSUPPORTED;
   return PKV_OK;
+}
+
+static int check_prefill_workspace(int64_t tiles, const void* workspace, size_t workspace_bytes) {
+  const size_t need = pkv::prefill_workspace_bytes(tiles);
+  if (need == 0) return PKV_OK;
+  if (workspace == nullptr || workspace_bytes < need) return PKV_E_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return PKV_E_INVALID_ARGUMENT;
+  return PKV_OK;
+}
+
+size_t pkv_prefill_workspace_bytes(int32_t batch, const int32_t* qo_indptr_h, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim) {
+  int max_qo = 0, total_q = 0;
+  int64_t tiles = 0;
+  // q / out are not needed to size the schedule: pass any aligned non-null stand-in
+  static const int32_t stand_in[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
+  if (check_prefill_common(stand_in, stand_in, stand_in, qo_indptr_h, batch, num_q_heads,
+                           num_kv_heads, head_dim, &max_qo, &total_q, &tiles) != PKV_OK)
+    return 0;
+  return pkv::prefill_workspace_bytes(tiles);
 }
 
 int pkv_ragged_prefill(const void* q, const void* k, const void* v, void* out,
                        const int32_t* qo_indptr, const int32_t* kv_indptr,
                        const int32_t* qo_indptr_h, const int32_t* kv_indptr_h, int32_t batch,
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t causal,
-                       float scale, void* stream) {
+                       float scale, void* workspace, size_t workspace_bytes, void* stream) {
   int max_qo = 0, total_q = 0;
+  int64_t tiles = 0;
   int st = check_prefill_common(q, out, qo_indptr, qo_indptr_h, batch, num_q_heads, num_kv_heads,
-                                head_dim, &max_qo, &total_q);
+                                head_dim, &max_qo, &total_q, &tiles);
   if (st != PKV_OK || batch == 0) return st;
   if (!kv_indptr_h || !kv_indptr) return PKV_E_INVALID_ARGUMENT;
   if (kv_indptr_h[0] != 0) return PKV_E_INVALID_ARGUMENT;
@@ -344,6 +375,8 @@ int pkv_ragged_prefill(const void* q, const void* k, const void* v, void* out,
   const int64_t total_kv = kv_indptr_h[batch];
   if (total_kv > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return PKV_E_INVALID_ARGUMENT;
   if (total_q == 0) return PKV_OK;
+  st = check_prefill_workspace(tiles, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
   pkv::PrefillArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -363,6 +396,8 @@ int pkv_ragged_prefill(const void* q, const void* k, const void* v, void* out,
   a.max_qo_len = max_qo;
   a.total_q = total_q;
   a.total_kv = total_kv;
+  a.tiles = tiles;
+  a.workspace = workspace;
   const hipError_t e = pkv::launch_ragged_prefill(a, (hipStream_t)stream);
   if (e == hipErrorNotSupported) return PKV_E_UNSUPPORTED;
   return hip_status(e);
@@ -373,13 +408,15 @@ int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* qo_indptr_h, const int32_t* kv_lens_h, void* out, int32_t batch,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                       int32_t num_blocks, int32_t max_blocks_per_seq, int32_t causal, float scale,
-                      void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream) {
   int max_qo = 0, total_q = 0;
+  int64_t tiles = 0;
   int st = check_prefill_common(q, out, qo_indptr, qo_indptr_h, batch, num_q_heads, num_kv_heads,
-                                head_dim, &max_qo, &total_q);
+                                head_dim, &max_qo, &total_q, &tiles);
   if (st != PKV_OK || batch == 0) return st;
   if (!block_size_ok(block_size)) return PKV_E_UNSUPPORTED;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PKV_E_INVALID_ARGUMENT;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PKV_E_UNSUPPORTED;
   if (!kv_lens_h || !kv_lens || !block_tables || !k_cache || !v_cache) return PKV_E_INVALID_ARGUMENT;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_E_INVALID_ARGUMENT;
   for (int b = 0; b < batch; ++b) {
@@ -387,6 +424,8 @@ int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
     if ((int64_t)kv_lens_h[b] > (int64_t)max_blocks_per_seq * block_size) return PKV_E_BAD_TABLE;
   }
   if (total_q == 0) return PKV_OK;
+  st = check_prefill_workspace(tiles, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
   pkv::PrefillArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -409,6 +448,8 @@ int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
   a.kv_lens_h = kv_lens_h;
   a.max_qo_len = max_qo;
   a.total_q = total_q;
+  a.tiles = tiles;
+  a.workspace = workspace;
   const hipError_t e = pkv::launch_paged_prefill(a, (hipStream_t)stream);
   if (e == hipErrorNotSupported) return PKV_E_UNSUPPORTED;
   return hip_status(e);

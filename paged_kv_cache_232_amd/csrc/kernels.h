@@ -67,10 +67,17 @@ struct PrefillArgs {
   const int32_t* qo_indptr_h;   // host copies (order the work-groups; may be null)
   const int32_t* kv_indptr_h;   // ragged only
   const int32_t* kv_lens_h;     // paged only
-  int max_qo_len;   // host-side maximum of the q lengths (sizes the grid)
+  int max_qo_len;   // host-side maximum of the q lengths
   int total_q;      // rows of q / out
   int64_t total_kv; // rows of k / v (ragged only)
+  int64_t tiles;    // (request, 128-row q tile) work items, from the host copies
+  void* workspace;  // >= prefill_workspace_bytes(tiles) bytes (the device-built schedule)
 };
+
+// (request, q tile) work items of a prefill launch, and the workspace its schedule needs (0 when
+// the schedule travels with the launch).
+int64_t prefill_tile_count(int batch, const int32_t* qo_indptr_h);
+size_t prefill_workspace_bytes(int64_t tiles);
 
 hipError_t launch_ragged_prefill(const PrefillArgs& a, hipStream_t stream);
 

@@ -37,12 +37,15 @@ namespace pkv {
 
 // Work-group schedule: entry y of the grid's y dimension is (request << 16 | q tile), sorted by
 // decreasing visible keys, so the hardware dispatcher starts the longest work first (greedy
-// longest-first list scheduling). n == 0: the plain (request, last-tile-first) grid instead.
+// longest-first list scheduling). Up to kMaxOrder entries are built on the host from the length
+// copies and passed by value; a longer schedule is built on the device by prefill_plan_kernel
+// into the caller's workspace (entries past the device's tile count read 0xffffffff: no work).
 constexpr int kMaxOrder = 768;
 struct TileOrder {
   int32_t n;
   uint32_t e[kMaxOrder];
 };
+constexpr uint32_t kNoTile = 0xffffffffu;
 
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
@@ -119,6 +122,40 @@ struct PrefillCfg {
   static_assert(ROWS_PER_LOAD <= 16, "a load instruction's rows must stay inside one block");
 };
 
+// The (request, q tile) a work-group runs and that request's extents, read from the device
+// copies of the offsets and clamped to the buffers the host sized (q / out hold total_q rows,
+// ragged k / v total_kv rows, a table row max_blocks blocks), so offsets that disagree with their
+// host copies give wrong rows, never an access outside those buffers. Returns false when the
+// work-group has nothing to do.
+struct TileWork {
+  int b, qt, q0, qo, kv;
+  int64_t kv0;
+};
+template <bool PAGED, int BM>
+__device__ __forceinline__ bool resolve_tile(int y, const TileOrder& order,
+                                             const uint32_t* __restrict__ order_dev,
+                                             const int32_t* __restrict__ qo_indptr,
+                                             const int32_t* __restrict__ kv_indptr,
+                                             const int32_t* __restrict__ kv_lens, int batch,
+                                             int total_q, int total_kv, int kv_cap, TileWork& t) {
+  const uint32_t sched = order_dev != nullptr ? order_dev[y] : order.e[min(y, kMaxOrder - 1)];
+  if (sched == kNoTile) return false;
+  t.b = (int)(sched >> 16);
+  t.qt = (int)(sched & 0xffffu);
+  if (t.b >= batch) return false;
+  t.q0 = clampi(qo_indptr[t.b], 0, total_q);
+  t.qo = clampi(qo_indptr[t.b + 1], t.q0, total_q) - t.q0;
+  if constexpr (PAGED) {
+    t.kv0 = 0;
+    t.kv = clampi(kv_lens[t.b], 0, kv_cap);
+  } else {
+    const int k0 = clampi(kv_indptr[t.b], 0, total_kv);
+    t.kv0 = k0;
+    t.kv = clampi(kv_indptr[t.b + 1], k0, total_kv) - k0;
+  }
+  return t.qt < (t.qo + BM - 1) / BM;
+}
+
 struct RaggedLoader {
   int64_t row0;  // first kv row of the request
   int Hkv, kh, D;
@@ -153,7 +190,8 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
                const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ tables,
                int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
-               int negate_q, int xcd_group, int xcd_heads, int n_rows, int bs_shift,
+               int negate_q, int xcd_group, int xcd_heads, int n_rows, int bs_shift, int batch,
+               int total_q, int total_kv, const uint32_t* __restrict__ order_dev,
                const TileOrder order) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
@@ -163,25 +201,17 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   int h, y;
   xcd_map(Hq, Hkv, G, xcd_group, xcd_heads, h, y);
   if (y >= n_rows) return;
-  const uint32_t sched = order.n > 0 ? order.e[min(y, kMaxOrder - 1)] : 0u;
-  const int b = order.n > 0 ? (int)(sched >> 16) : y;
+  TileWork tw;
+  if (!resolve_tile<PAGED, kBM>(y, order, order_dev, qo_indptr, kv_indptr, kv_lens, batch, total_q,
+                                total_kv, max_blocks * BS, tw))
+    return;
+  const int b = tw.b;
   const int kh = h / G;
-
-  const int q0 = qo_indptr[b];
-  const int qo = qo_indptr[b + 1] - q0;
-  int kv;
-  int64_t kv0 = 0;
-  if constexpr (PAGED) {
-    kv = clampi(kv_lens[b], 0, max_blocks * BS);
-  } else {
-    kv0 = kv_indptr[b];
-    kv = kv_indptr[b + 1] - (int)kv0;
-  }
-  const int n_qt = (qo + kBM - 1) / kBM;
-  // scheduled tile, or the plain grid's last tile first
-  const int qt = order.n > 0 ? (int)(sched & 0xffffu) : n_qt - 1 - (int)blockIdx.z;
-  if (qt < 0 || qt >= n_qt) return;
-  const int m0 = qt * kBM;
+  const int q0 = tw.q0;
+  const int qo = tw.qo;
+  const int kv = tw.kv;
+  const int64_t kv0 = tw.kv0;
+  const int m0 = tw.qt * kBM;
   const int off = kv - qo;  // row i sits at key position i + off
 
   // keys this tile can see: [0, kv_end)
@@ -453,8 +483,9 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
                  const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ tables,
                  int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
-                 int negate_q, int xcd_group, int xcd_heads, int n_rows, int bs_shift,
-               const TileOrder order) {
+                 int negate_q, int xcd_group, int xcd_heads, int n_rows, int bs_shift, int batch,
+                 int total_q, int total_kv, const uint32_t* __restrict__ order_dev,
+                 const TileOrder order) {
   using C = P16Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
   // buffer j (0/1): K rows at smem + j*BUF, V rows BN*RSE further; the output tile reuses it
@@ -463,25 +494,17 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   int h, y;
   xcd_map(Hq, Hkv, G, xcd_group, xcd_heads, h, y);
   if (y >= n_rows) return;
-  const uint32_t sched = order.n > 0 ? order.e[min(y, kMaxOrder - 1)] : 0u;
-  const int b = order.n > 0 ? (int)(sched >> 16) : y;
+  TileWork tw;
+  if (!resolve_tile<PAGED, kP16BM>(y, order, order_dev, qo_indptr, kv_indptr, kv_lens, batch,
+                                   total_q, total_kv, max_blocks * BS, tw))
+    return;
+  const int b = tw.b;
   const int kh = h / G;
-
-  const int q0 = qo_indptr[b];
-  const int qo = qo_indptr[b + 1] - q0;
-  int kv;
-  int64_t kv0 = 0;
-  if constexpr (PAGED) {
-    kv = clampi(kv_lens[b], 0, max_blocks * BS);
-  } else {
-    kv0 = kv_indptr[b];
-    kv = kv_indptr[b + 1] - (int)kv0;
-  }
-  const int n_qt = (qo + kP16BM - 1) / kP16BM;
-  // scheduled tile, or the plain grid's last tile first
-  const int qt = order.n > 0 ? (int)(sched & 0xffffu) : n_qt - 1 - (int)blockIdx.z;
-  if (qt < 0 || qt >= n_qt) return;
-  const int m0 = qt * kP16BM;
+  const int q0 = tw.q0;
+  const int qo = tw.qo;
+  const int kv = tw.kv;
+  const int64_t kv0 = tw.kv0;
+  const int m0 = tw.qt * kP16BM;
   const int off = kv - qo;  // row i sits at key position i + off
 
   int kv_end = kv;
@@ -702,12 +725,28 @@ constexpr bool use_p16() {
   return D >= 256;
 }
 
+// Keys a (request, q tile)'s rows can see: the work the longest-first schedule sorts by.
+static int64_t tile_work(int qo, int64_t kv, int qt, int causal) {
+  int64_t vis = kv;
+  if (causal) vis = std::min<int64_t>(kv, (int64_t)(qt + 1) * kBM + kv - qo);
+  return std::max<int64_t>(vis, 0);
+}
+
+int64_t prefill_tile_count(int batch, const int32_t* qo_indptr_h) {
+  int64_t n = 0;
+  for (int b = 0; b < batch; ++b) n += (qo_indptr_h[b + 1] - qo_indptr_h[b] + kBM - 1) / kBM;
+  return n;
+}
+
+static size_t align256p(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t prefill_workspace_bytes(int64_t tiles) {
+  return tiles <= kMaxOrder ? 0 : align256p((size_t)tiles * sizeof(uint32_t));
+}
+
 // Longest-first schedule of the (request, q tile) work-groups from the host copies of the
-// lengths: work = keys a tile's rows can see. Empty when a copy is missing or there are more
-// tiles than the schedule holds.
+// lengths, for launches of at most kMaxOrder tiles (passed by value with the launch).
 static void build_order(const PrefillArgs& a, TileOrder& ord) {
-  ord.n = 0;
-  if (a.qo_indptr_h == nullptr || (a.kv_indptr_h == nullptr && a.kv_lens_h == nullptr)) return;
   struct Item {
     int64_t work;
     uint32_t e;
@@ -715,16 +754,12 @@ static void build_order(const PrefillArgs& a, TileOrder& ord) {
   std::vector<Item> items;
   for (int b = 0; b < a.batch; ++b) {
     const int qo = a.qo_indptr_h[b + 1] - a.qo_indptr_h[b];
-    int64_t kv = a.kv_indptr_h ? (int64_t)a.kv_indptr_h[b + 1] - a.kv_indptr_h[b]
-                               : std::min<int64_t>(std::max(a.kv_lens_h[b], 0),
-                                                   (int64_t)a.max_blocks_per_seq * a.block_size);
+    const int64_t kv = a.kv_indptr_h ? (int64_t)a.kv_indptr_h[b + 1] - a.kv_indptr_h[b]
+                                     : std::min<int64_t>(std::max(a.kv_lens_h[b], 0),
+                                                         (int64_t)a.max_blocks_per_seq * a.block_size);
     const int n_qt = (qo + kBM - 1) / kBM;
-    if (n_qt > 0xffff || (int)items.size() + n_qt > kMaxOrder) return;
-    for (int qt = 0; qt < n_qt; ++qt) {
-      int64_t vis = kv;
-      if (a.causal) vis = std::min<int64_t>(kv, (int64_t)(qt + 1) * kBM + kv - qo);
-      items.push_back({std::max<int64_t>(vis, 0), ((uint32_t)b << 16) | (uint32_t)qt});
-    }
+    for (int qt = 0; qt < n_qt; ++qt)
+      items.push_back({tile_work(qo, kv, qt, a.causal), ((uint32_t)b << 16) | (uint32_t)qt});
   }
   std::stable_sort(items.begin(), items.end(),
                    [](const Item& x, const Item& y) { return x.work > y.work; });
@@ -732,37 +767,127 @@ static void build_order(const PrefillArgs& a, TileOrder& ord) {
   ord.n = (int)items.size();
 }
 
+// Device-built longest-first schedule for launches of more tiles than the by-value list holds:
+// one work-group counts the tiles per work bucket (visible keys in units of 32, most first),
+// scans the counts and scatters each tile's entry to its bucket's range of the workspace. Tiles
+// of one bucket land in any order (each tile's result does not depend on its slot). Entries
+// [device tile count, capacity) read kNoTile; tiles beyond capacity (device offsets that
+// disagree with their host copies) are dropped.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 4096;
+constexpr int kPlanPerThread = kPlanBuckets / kPlanThreads;
+
+__global__ void __launch_bounds__(kPlanThreads)
+prefill_plan_kernel(const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
+                    const int32_t* __restrict__ kv_lens, int batch, int causal, int total_q,
+                    int total_kv, int kv_cap, uint32_t* __restrict__ order, int capacity) {
+  __shared__ int hist[kPlanBuckets];
+  __shared__ int wave_sum[kPlanThreads / kWave];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kPlanBuckets; i += kPlanThreads) hist[i] = 0;
+  __syncthreads();
+  auto extents = [&](int b, int& qo, int& kv) {
+    const int q0 = clampi(qo_indptr[b], 0, total_q);
+    qo = clampi(qo_indptr[b + 1], q0, total_q) - q0;
+    if (kv_lens != nullptr) {
+      kv = clampi(kv_lens[b], 0, kv_cap);
+    } else {
+      const int k0 = clampi(kv_indptr[b], 0, total_kv);
+      kv = clampi(kv_indptr[b + 1], k0, total_kv) - k0;
+    }
+  };
+  auto bucket = [&](int qo, int kv, int qt) {
+    int vis = kv;
+    if (causal) vis = (int)clampi<int64_t>((int64_t)(qt + 1) * kBM + kv - qo, 0, kv);
+    return kPlanBuckets - 1 - min((vis + 31) >> 5, kPlanBuckets - 1);
+  };
+  for (int b = tid; b < batch; b += kPlanThreads) {
+    int qo, kv;
+    extents(b, qo, kv);
+    const int n_qt = min((qo + kBM - 1) / kBM, 0xffff);
+    for (int qt = 0; qt < n_qt; ++qt) atomicAdd(&hist[bucket(qo, kv, qt)], 1);
+  }
+  __syncthreads();
+  // exclusive scan: each thread owns kPlanPerThread consecutive buckets
+  int local[kPlanPerThread];
+  int run = 0;
+#pragma unroll
+  for (int j = 0; j < kPlanPerThread; ++j) {
+    local[j] = run;
+    run += hist[tid * kPlanPerThread + j];
+  }
+  const int lane = tid & (kWave - 1);
+  int incl = run;
+#pragma unroll
+  for (int s = 1; s < kWave; s <<= 1) {
+    const int o = __shfl_up(incl, s, kWave);
+    if (lane >= s) incl += o;
+  }
+  if (lane == kWave - 1) wave_sum[tid / kWave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int wv = 0; wv < tid / kWave; ++wv) before += wave_sum[wv];
+  int total = 0;
+  for (int wv = 0; wv < kPlanThreads / kWave; ++wv) total += wave_sum[wv];
+  const int start = before + incl - run;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPlanPerThread; ++j) hist[tid * kPlanPerThread + j] = start + local[j];
+  __syncthreads();
+  for (int b = tid; b < batch; b += kPlanThreads) {
+    int qo, kv;
+    extents(b, qo, kv);
+    const int n_qt = min((qo + kBM - 1) / kBM, 0xffff);
+    for (int qt = 0; qt < n_qt; ++qt) {
+      const int pos = atomicAdd(&hist[bucket(qo, kv, qt)], 1);
+      if (pos < capacity) order[pos] = ((uint32_t)b << 16) | (uint32_t)qt;
+    }
+  }
+  for (int i = total + tid; i < capacity; i += kPlanThreads) order[i] = kNoTile;
+}
+
 template <int D, bool PAGED>
 static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
-  const int n_qt = (a.max_qo_len + kBM - 1) / kBM;
-  if (n_qt == 0) return hipSuccess;
+  if (a.tiles == 0) return hipSuccess;
   TileOrder order;
-  build_order(a, order);
+  order.n = 0;
+  const uint32_t* order_dev = nullptr;
+  const int kv_cap = PAGED ? a.max_blocks_per_seq * a.block_size : 0;
+  if (a.tiles <= kMaxOrder) {
+    build_order(a, order);
+  } else {
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.qo_indptr,
+                       a.kv_indptr, a.kv_lens, a.batch, a.causal, a.total_q, (int)a.total_kv, kv_cap,
+                       (uint32_t*)a.workspace, (int)a.tiles);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    order_dev = (const uint32_t*)a.workspace;
+  }
   const bool q8 = a.num_q_heads % 8 == 0;
   const int xcd_group = (q8 && 8 % a.num_kv_heads == 0) ? 8 / a.num_kv_heads : 0;
   const int xcd_heads = (q8 && xcd_group == 0) ? a.num_q_heads / 8 : 0;
-  const int n_rows = order.n > 0 ? order.n : a.batch;
+  const int n_rows = (int)a.tiles;
   const int grid_rows = xcd_group > 0 ? (n_rows + xcd_group - 1) / xcd_group * xcd_group : n_rows;
   float scale_log2 = a.scale * kLog2e;
   const int negate_q = scale_log2 < 0.f;
   if (negate_q) scale_log2 = -scale_log2;
   if (!(scale_log2 >= 1.17549435e-38f)) scale_log2 = 1.17549435e-38f;  // zero (or denormal) scale
-  const dim3 grid = order.n > 0 ? dim3(a.num_q_heads, grid_rows, 1) : dim3(a.num_q_heads, grid_rows, n_qt);
+  const dim3 grid(a.num_q_heads, grid_rows, 1);
   const int bs_shift = a.block_size > 0 ? __builtin_ctz((unsigned)a.block_size) : 0;
   if constexpr (use_p16<D>()) {
     hipLaunchKernelGGL((prefill16_kernel<D, PAGED>), grid, dim3(kP16Threads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
                        a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
-                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_group, xcd_heads, n_rows, bs_shift,
-                       order);
+                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_group, xcd_heads,
+                       n_rows, bs_shift, a.batch, a.total_q, (int)a.total_kv, order_dev, order);
   } else {
     hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(kPrefillThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
                        a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
-                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_group, xcd_heads, n_rows, bs_shift,
-                       order);
+                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_group, xcd_heads,
+                       n_rows, bs_shift, a.batch, a.total_q, (int)a.total_kv, order_dev, order);
   }
   return hipGetLastError();
 }

@@ -24,7 +24,7 @@ def _declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = pkv.load_library()
     syms = _declared_symbols()
-    assert len(syms) == 17, syms
+    assert len(syms) == 18, syms
     for s in syms:
         assert hasattr(lib, s), f"{s} missing from libpkv.so"
     assert set(syms) == set(pkv._SIGNATURES), "binding and header disagree"
@@ -81,14 +81,55 @@ def test_argument_errors_return_before_launch():
     # prefill: indptr checks run on the host copies
     qi = (ctypes.c_int32 * 3)(0, 5, 3)  # decreasing
     ki = (ctypes.c_int32 * 3)(0, 5, 9)
-    assert lib.pkv_ragged_prefill(fake, fake, fake, fake, fake, fake, qi, ki, 2, 4, 2, 128, 1, 1.0, nul) \
+    assert lib.pkv_ragged_prefill(fake, fake, fake, fake, fake, fake, qi, ki, 2, 4, 2, 128, 1, 1.0, nul, 0, nul) \
         == pkv.E_INVALID_ARGUMENT
     qi = (ctypes.c_int32 * 3)(0, 5, 9)
-    assert lib.pkv_ragged_prefill(fake, fake, fake, fake, fake, fake, qi, ki, 2, 4, 2, 80, 1, 1.0, nul) \
+    assert lib.pkv_ragged_prefill(fake, fake, fake, fake, fake, fake, qi, ki, 2, 4, 2, 80, 1, 1.0, nul, 0, nul) \
         == pkv.E_UNSUPPORTED
     kl = (ctypes.c_int32 * 2)(5, 100)
     assert lib.pkv_paged_prefill(fake, fake, fake, fake, fake, fake, qi, kl, fake, 2, 4, 2, 128, 16, 64, 4, 1,
-                                 1.0, nul) == pkv.E_BAD_TABLE  # 100 tokens > 4 blocks * 16
+                                 1.0, nul, 0, nul) == pkv.E_BAD_TABLE  # 100 tokens > 4 blocks * 16
+
+
+def _indptr(lens):
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
+
+def test_prefill_workspace_bytes_and_errors():
+    """Up to 768 (request, 128-row q tile) items the schedule travels with the launch (no workspace);
+    beyond, one 32-bit entry per item, 256-byte aligned. Too small a workspace is reported before any
+    launch; so are schedules the grid cannot hold."""
+    lib = pkv.load_library()
+    nul = None
+    fake = ctypes.c_void_p(1 << 20)
+    small = _indptr([128] * 768)                      # 768 tiles
+    assert pkv.prefill_workspace_bytes(small, 32, 8, 128) == 0
+    big = _indptr([1] * 800 + [129])                  # 802 tiles
+    assert pkv.prefill_workspace_bytes(big, 32, 8, 128) == (802 * 4 + 255) // 256 * 256
+    # arguments the calls reject size nothing
+    assert pkv.prefill_workspace_bytes(big, 32, 8, 96) == 0
+    assert pkv.prefill_workspace_bytes(_indptr([]), 32, 8, 128) == 0
+    bp = big.ctypes.data_as(ctypes.c_void_p)
+    kvb = _indptr([37] * 800 + [129])
+    kp = kvb.ctypes.data_as(ctypes.c_void_p)
+    B = len(big) - 1
+    need = pkv.prefill_workspace_bytes(big, 8, 2, 128)
+    assert lib.pkv_ragged_prefill(fake, fake, fake, fake, fake, fake, bp, kp, B, 8, 2, 128, 1, 1.0, nul, 0, nul) \
+        == pkv.E_WORKSPACE_TOO_SMALL
+    assert lib.pkv_ragged_prefill(fake, fake, fake, fake, fake, fake, bp, kp, B, 8, 2, 128, 1, 1.0, fake,
+                                  need - 1, nul) == pkv.E_WORKSPACE_TOO_SMALL
+    kl = np.full(B, 50, np.int32)
+    assert lib.pkv_paged_prefill(fake, fake, fake, fake, fake, fake, bp, kl.ctypes.data_as(ctypes.c_void_p), fake,
+                                 B, 8, 2, 128, 16, 64, 4, 1, 1.0, fake, need - 1, nul) == pkv.E_WORKSPACE_TOO_SMALL
+    # more q tiles than one launch's grid holds, and more than 65535 requests
+    huge = _indptr([128 * 1000] * 66)                 # 66000 tiles
+    hp = huge.ctypes.data_as(ctypes.c_void_p)
+    assert lib.pkv_ragged_prefill(fake, fake, fake, fake, fake, fake, hp, hp, 66, 8, 2, 128, 1, 1.0, fake,
+                                  1 << 30, nul) == pkv.E_UNSUPPORTED
+    many = _indptr([1] * 65536)
+    mp = many.ctypes.data_as(ctypes.c_void_p)
+    assert lib.pkv_ragged_prefill(fake, fake, fake, fake, fake, fake, mp, mp, 65536, 8, 2, 128, 1, 1.0, fake,
+                                  1 << 30, nul) == pkv.E_UNSUPPORTED
 
 
 def test_workspace_bytes():

@@ -27,7 +27,8 @@ def test_chunked_prefill_config_scatter_bit_exact():
     _scatter_and_compare(make_config(5))
 
 
-@pytest.mark.parametrize("hq,hkv,d,bs", [(4, 1, 64, 16), (8, 8, 128, 16), (4, 2, 256, 32), (2, 2, 128, 64)])
+@pytest.mark.parametrize("hq,hkv,d,bs", [(4, 1, 64, 16), (8, 8, 128, 16), (4, 2, 256, 32), (2, 2, 128, 64),
+                                         (8, 2, 128, 128), (4, 4, 256, 256), (2, 1, 64, 256)])
 def test_scatter_shapes_and_skipped_slots(hq, hkv, d, bs):
     ci = chunked_prefill_inputs(300 + d + bs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, chunk_lens=[1, 37, 16],
                                 prefix_lens=[5, 0, 16], block_size=bs, num_blocks=None)

@@ -33,15 +33,16 @@ RAGGED_EDGE = [
     ([513, 255, 256], None, 4, 1, 128, True),       # several 256-row q tiles, ragged tails
     ([700, 31], [1500, 31], 2, 2, 64, True),        # long prefix offset, head_dim 64
     ([600, 90], [600, 4000], 4, 2, 128, False),     # non-causal, kv much longer than q
-    ([1] * 800, [37] * 800, 2, 1, 64, True),         # more q tiles than the launch schedule holds
+    ([1] * 800, [37] * 800, 2, 1, 64, True),         # more q tiles than the launch arguments hold:
+                                                    # schedule built on the device in the workspace
     # XCD placement of work-groups: heads of one kv head grouped on an XCD over 8 / Hkv schedule
-    # rows (row counts not a multiple of the group pad the grid), the per-XCD head mapping when
-    # Hkv does not divide 8, and the plain grid
+    # rows (row counts not a multiple of the group pad the grid), and the per-XCD head mapping
+    # when Hkv does not divide 8
     ([130, 70, 260], None, 16, 16, 128, True),      # Hkv = 16: per-XCD heads
     ([200, 17], None, 24, 3, 64, True),             # Hkv = 3: per-XCD heads, head_dim 64
     ([129, 5, 300], None, 8, 1, 128, True),         # group of 8 rows, 6 rows used
     ([129, 40, 1], [129, 90, 1], 16, 4, 256, True), # group of 2 rows, 4 rows, head_dim 256
-    ([1] * 801, [37] * 801, 8, 2, 128, True),       # plain grid (801 requests), group of 4
+    ([1] * 801, [37] * 801, 8, 2, 128, True),       # device-built schedule, groups of 4 rows
 ]
 
 
@@ -74,51 +75,56 @@ def _chunked(ci):
 
 
 PAGED_EDGE = [
-    # chunk_lens, prefix_lens, Hq, Hkv, D, BS
-    ([1], [0], 1, 1, 64, 16),
-    ([64, 1, 130], [0, 17, 31], 4, 2, 128, 16),
-    ([9, 200], [300, 0], 8, 2, 256, 16),
-    ([50, 129], [16, 100], 4, 1, 128, 32),
-    ([33], [5000], 2, 2, 64, 64),
-    ([600, 257], [700, 0], 4, 2, 128, 16),
-    ([9, 200, 129], [300, 0, 2000], 16, 4, 256, 16),  # 5 schedule rows in groups of 2
-    ([77, 1, 256], [33, 4000, 16], 8, 1, 64, 16),     # groups of 8, head_dim 64
-    ([140, 60], [900, 45], 32, 8, 128, 32),           # one row per group
+    # chunk_lens, prefix_lens, Hq, Hkv, D, BS, causal
+    ([1], [0], 1, 1, 64, 16, True),
+    ([64, 1, 130], [0, 17, 31], 4, 2, 128, 16, True),
+    ([9, 200], [300, 0], 8, 2, 256, 16, True),
+    ([50, 129], [16, 100], 4, 1, 128, 32, True),
+    ([33], [5000], 2, 2, 64, 64, True),
+    ([600, 257], [700, 0], 4, 2, 128, 16, True),
+    ([9, 200, 129], [300, 0, 2000], 16, 4, 256, 16, True),  # 5 schedule rows in groups of 2
+    ([77, 1, 256], [33, 4000, 16], 8, 1, 64, 16, True),     # groups of 8, head_dim 64
+    ([140, 60], [900, 45], 32, 8, 128, 32, True),           # one row per group
+    # blocks larger than a kv tile (64 keys at head_dim <= 128, 32 at 256): a tile's rows sit in
+    # one block at an offset, and the last blocks are partly filled
+    ([130, 7], [300, 1000], 8, 2, 128, 128, True),
+    ([66, 200], [129, 511], 4, 4, 64, 256, True),
+    ([150, 40], [257, 1500], 16, 4, 256, 128, True),
+    ([33, 140], [700, 3], 4, 1, 256, 256, True),
+    ([200, 70, 1], [300, 0, 40], 8, 2, 128, 128, True),
+    # non-causal: every query row sees the whole prefix and chunk
+    ([100, 140], [250, 33], 4, 2, 128, 16, False),
+    ([60, 129], [1000, 0], 16, 4, 256, 16, False),
+    ([31, 90], [64, 700], 8, 2, 64, 128, False),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(PAGED_EDGE)))
 def test_paged_prefill_edge_shapes(case):
-    C, P, hq, hkv, d, bs = PAGED_EDGE[case]
+    C, P, hq, hkv, d, bs, causal = PAGED_EDGE[case]
     ci = chunked_prefill_inputs(3000 + case, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, chunk_lens=C,
-                                prefix_lens=P, block_size=bs)
+                                prefix_lens=P, block_size=bs, causal=causal)
     out, kc, vc = _chunked(ci)
     ek, ev = oracle.reshape_and_cache(ci.k_new, ci.v_new, ci.k_cache, ci.v_cache, ci.slot_mapping)
     assert np.array_equal(kc.view(torch.int16).numpy(), ek) and np.array_equal(vc.view(torch.int16).numpy(), ev)
     ref = oracle.paged_prefill(ci.q, torch.from_numpy(ek).view(torch.bfloat16), torch.from_numpy(ev).view(torch.bfloat16),
-                               ci.block_tables, ci.qo_indptr, ci.kv_lens, True, ci.scale)
+                               ci.block_tables, ci.qo_indptr, ci.kv_lens, ci.causal, ci.scale)
     assert_parity(out, ref, f"paged edge {PAGED_EDGE[case]}")
 
 
-def test_chunked_prefill_config_sampled():
-    """16 requests, prefix up to 4096, head_dim 256: scatter checked bit-exact on the whole pool, attention
-    checked on sampled rows (every request's first and last row plus random rows)."""
+def test_chunked_prefill_config_full():
+    """16 requests, prefix up to 4096, head_dim 256, at the launch the benchmark times: the scatter
+    bit-exact on the whole pool, every output row against the oracle, and a second run identical."""
     ci = make_config(5)
     out, kc, vc = _chunked(ci)
     ek, ev = oracle.reshape_and_cache(ci.k_new, ci.v_new, ci.k_cache, ci.v_cache, ci.slot_mapping)
     assert np.array_equal(kc.view(torch.int16).numpy(), ek) and np.array_equal(vc.view(torch.int16).numpy(), ev)
-    rng = np.random.default_rng(5)
-    qi = ci.qo_indptr.tolist()
-    rows = []
-    for b in range(len(qi) - 1):
-        for t in (qi[b], qi[b + 1] - 1, int(rng.integers(qi[b], qi[b + 1]))):
-            rows.append((t, int(rng.integers(0, 16))))
-    ref = oracle.paged_prefill_rows(ci.q, torch.from_numpy(ek).view(torch.bfloat16),
-                                    torch.from_numpy(ev).view(torch.bfloat16), ci.block_tables, ci.qo_indptr,
-                                    ci.kv_lens, True, ci.scale, rows)
-    got = torch.stack([out[t, h] for t, h in rows])
-    print("config5 sampled", assert_parity(got, ref, "config5 sampled"))
-    assert torch.isfinite(out.float()).all()
+    ref = oracle.paged_prefill(ci.q, torch.from_numpy(ek).view(torch.bfloat16),
+                               torch.from_numpy(ev).view(torch.bfloat16), ci.block_tables, ci.qo_indptr,
+                               ci.kv_lens, ci.causal, ci.scale)
+    print("config5 full", assert_parity(out, ref, "config5 paged prefill"))
+    out2, _, _ = _chunked(ci)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "run-to-run difference"
 
 
 def test_paged_prefill_with_empty_prefix_equals_ragged():
@@ -130,3 +136,101 @@ def test_paged_prefill_with_empty_prefix_equals_ragged():
                              ci.qo_indptr.to(DEV), True, ci.scale, qo_indptr_h=ci.qo_indptr, kv_indptr_h=ci.qo_indptr)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), rag.cpu().view(torch.int16))
+
+
+def test_ragged_prefill_device_schedule_many_tiles():
+    """3 000 (request, q tile) items of mixed lengths: the longest-first order is built on the device in
+    the caller's workspace (items of one work bucket land in any order); every row matches the oracle
+    and a second run (another order inside the buckets) is identical bit for bit."""
+    g = torch.Generator().manual_seed(11)
+    qo = [int(x) for x in torch.randint(1, 300, (1900,), generator=g)]
+    ri = ragged_prefill_inputs(2100, num_q_heads=8, num_kv_heads=2, head_dim=64, qo_lens=qo, causal=True)
+    need = pkv.prefill_workspace_bytes(ri.qo_indptr, 8, 2, 64)
+    tiles = sum((n + 127) // 128 for n in qo)
+    assert tiles > 768 and need >= 4 * tiles
+    ref = oracle.ragged_prefill(ri.q, ri.k, ri.v, ri.qo_indptr, ri.kv_indptr, ri.causal, ri.scale)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device=DEV)  # contents need no initialisation
+    args = (ri.q.to(DEV), ri.k.to(DEV), ri.v.to(DEV), ri.qo_indptr.to(DEV), ri.kv_indptr.to(DEV), True, ri.scale)
+    out = pkv.ragged_prefill(*args, qo_indptr_h=ri.qo_indptr, kv_indptr_h=ri.kv_indptr, workspace=ws)
+    torch.cuda.synchronize()
+    print("device schedule", assert_parity(out.cpu(), ref, "device-built schedule"))
+    out2 = pkv.ragged_prefill(*args, qo_indptr_h=ri.qo_indptr, kv_indptr_h=ri.kv_indptr, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+GUARD = 512  # rows of sentinel before and after each buffer the kernels are told about
+
+
+def _guarded(t: torch.Tensor):
+    """t placed in a larger device buffer between GUARD sentinel rows; returns (buffer, view of t)."""
+    buf = torch.full((t.shape[0] + 2 * GUARD,) + tuple(t.shape[1:]), 7.0, dtype=t.dtype)
+    buf[GUARD:GUARD + t.shape[0]] = t
+    buf = buf.to(DEV)
+    return buf, buf[GUARD:GUARD + t.shape[0]]
+
+
+def _guards_intact(buf: torch.Tensor):
+    b = buf.cpu().float()
+    return bool((b[:GUARD] == 7.0).all()) and bool((b[-GUARD:] == 7.0).all())
+
+
+def test_ragged_prefill_device_offsets_clamped_to_host_sizes():
+    """Device offsets that disagree with their host copies (the last ones past the buffers' ends) are
+    clamped to the rows the host copies describe: the output equals the oracle over the clamped
+    extents and no sentinel row around q, k, v or out changes."""
+    qo_h, kv_h = [100, 150], [90, 210]
+    ri = ragged_prefill_inputs(2200, num_q_heads=4, num_kv_heads=2, head_dim=128, qo_lens=qo_h, kv_lens=kv_h)
+    qi_dev = torch.tensor([0, 120, 300], dtype=torch.int32)    # host: [0, 100, 250]
+    ki_dev = torch.tensor([0, 95, 340], dtype=torch.int32)     # host: [0, 90, 300]
+    qb, q = _guarded(ri.q)
+    kb, k = _guarded(ri.k)
+    vb, v = _guarded(ri.v)
+    ob, out = _guarded(torch.zeros_like(ri.q))
+    pkv.ragged_prefill(q, k, v, qi_dev.to(DEV), ki_dev.to(DEV), True, ri.scale, qo_indptr_h=ri.qo_indptr,
+                       kv_indptr_h=ri.kv_indptr, out=out)
+    torch.cuda.synchronize()
+    for b_ in (qb, kb, vb, ob):
+        assert _guards_intact(b_), "a sentinel row changed"
+    qi_c = torch.tensor([0, 120, 250], dtype=torch.int32)
+    ki_c = torch.tensor([0, 95, 300], dtype=torch.int32)
+    ref = oracle.ragged_prefill(ri.q, ri.k, ri.v, qi_c, ki_c, True, ri.scale)
+    assert_parity(out.cpu(), ref, "clamped ragged offsets")
+
+
+def test_paged_prefill_device_lengths_clamped():
+    """A device kv length beyond its table row's capacity and a device q offset past the end of q are
+    clamped: the output equals the oracle over the clamped extents, sentinel rows stay intact."""
+    ci = chunked_prefill_inputs(2300, num_q_heads=8, num_kv_heads=2, head_dim=128, chunk_lens=[60, 100],
+                                prefix_lens=[4, 28], block_size=16)
+    # every table row full: kv lengths 64 and 128 fill 4 and 8 blocks of 16
+    assert ci.kv_lens.tolist() == [64, 128] and ci.block_tables.shape[1] == 8
+    kc, vc = ci.k_cache.to(DEV), ci.v_cache.to(DEV)
+    pkv.reshape_and_cache(ci.k_new.to(DEV), ci.v_new.to(DEV), kc, vc, ci.slot_mapping.to(DEV))
+    qb, q = _guarded(ci.q)
+    ob, out = _guarded(torch.zeros_like(ci.q))
+    qi_dev = torch.tensor([0, 60, 200], dtype=torch.int32)     # host: [0, 60, 160]
+    kl_dev = torch.tensor([64, 5000], dtype=torch.int32)       # host: [64, 128]; capacity 8 * 16
+    pkv.paged_prefill(q, kc, vc, ci.block_tables.to(DEV), qi_dev.to(DEV), kl_dev.to(DEV), True, ci.scale,
+                      qo_indptr_h=ci.qo_indptr, kv_lens_h=ci.kv_lens, out=out)
+    torch.cuda.synchronize()
+    assert _guards_intact(qb) and _guards_intact(ob), "a sentinel row changed"
+    ek, ev = oracle.reshape_and_cache(ci.k_new, ci.v_new, ci.k_cache, ci.v_cache, ci.slot_mapping)
+    ref = oracle.paged_prefill(ci.q, torch.from_numpy(ek).view(torch.bfloat16), torch.from_numpy(ev).view(torch.bfloat16),
+                               ci.block_tables, ci.qo_indptr, ci.kv_lens, True, ci.scale)
+    assert_parity(out.cpu(), ref, "clamped paged lengths")
+
+
+def test_prefill_rejects_misshaped_outputs_and_workspaces():
+    ri = ragged_prefill_inputs(2400, num_q_heads=4, num_kv_heads=2, head_dim=64, qo_lens=[10, 20])
+    args = (ri.q.to(DEV), ri.k.to(DEV), ri.v.to(DEV), ri.qo_indptr.to(DEV), ri.kv_indptr.to(DEV), True, ri.scale)
+    with pytest.raises(ValueError):
+        pkv.ragged_prefill(*args, out=torch.empty(29, 4, 64, dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        pkv.ragged_prefill(*args, out=torch.empty(30, 4, 32, dtype=torch.bfloat16, device=DEV))
+    big = ragged_prefill_inputs(2401, num_q_heads=2, num_kv_heads=1, head_dim=64, qo_lens=[1] * 800)
+    need = pkv.prefill_workspace_bytes(big.qo_indptr, 2, 1, 64)
+    with pytest.raises(ValueError):
+        pkv.ragged_prefill(big.q.to(DEV), big.k.to(DEV), big.v.to(DEV), big.qo_indptr.to(DEV),
+                           big.kv_indptr.to(DEV), True, big.scale, workspace=torch.empty(need - 4, dtype=torch.uint8,
+                                                                                         device=DEV))
