@@ -116,6 +116,26 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attn_decode without a workspace, for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). Same arguments, paths and
+ * results as pkv_paged_attn_decode, less workspace / workspace_bytes: the split-KV partials live
+ * in a 64 MiB device array the library holds (one per GPU it runs on, kept until the process
+ * ends; its address is looked up on the device's first call). The call itself allocates nothing.
+ *   - A shape whose partials exceed 64 MiB (pkv_decode_workspace_bytes(...) > 64 << 20) is
+ *     PKV_E_WORKSPACE_TOO_SMALL, before anything is enqueued.
+ *   - `stream` must belong to the current device (else PKV_E_INVALID_ARGUMENT).
+ *   - Every call on one GPU shares that GPU's array and leaves its partials there. Calls that
+ *     overlap on one GPU (other streams, other host threads) race on it: order them on one stream.
+ */
+int pkv_paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                                  float* lse, int32_t batch, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, int32_t max_blocks_per_seq,
+                                  int32_t max_seq_len, float scale, int32_t partition_tokens,
+                                  void* stream);
+
+/*
  * ragged_prefill — N requests' attention in one launch over contiguous ragged rows.
  * Defined by the spark_runtime/flashinfer.rs page, ragged_prefill_bf16_hd256 and its CPU-reference
  * test: request b's queries are rows qo_indptr[b]..qo_indptr[b+1] of q, its keys/values rows

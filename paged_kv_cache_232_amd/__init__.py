@@ -37,6 +37,9 @@ _SIGNATURES = {
     "pkv_paged_attn_decode": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                              _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                              _c_i32, _c_f32, _c_i32, _c_ptr, _c_size, _c_ptr]),
+    "pkv_paged_attn_decode_noalloc": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                                     _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                     _c_i32, _c_f32, _c_i32, _c_ptr]),
     "pkv_ragged_prefill": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                           _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                           _c_ptr, _c_size, _c_ptr]),
@@ -229,6 +232,34 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                                      block_tables.shape[1], int(max_seq_len), float(scale),
                                      int(partition_tokens), _ptr(workspace), wbytes, _stream(q)),
            "paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                              *, max_seq_len: int, partition_tokens: int = -1,
+                              lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """paged_attn_decode through pkv_paged_attn_decode_noalloc: the split partials live in the library's
+    per-GPU device array, so neither this call nor the library allocates. ``out`` (and ``lse``) are the
+    caller's; ``max_seq_len`` is required (no device sync). bf16 caches."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, 3, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    NB, Hkv, BS, D2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or D2 != D or block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("decode shapes disagree")
+    _need_out(out, "out", torch.bfloat16, (B, Hq, D), dev)
+    if lse is not None:
+        _need_out(lse, "lse", torch.float32, (B, Hq), dev)
+    _check(lib.pkv_paged_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                             _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, D, BS, NB,
+                                             block_tables.shape[1], int(max_seq_len), float(scale),
+                                             int(partition_tokens), _stream(q)), "paged_attn_decode_noalloc")
     return out
 
 

@@ -14,7 +14,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkv.so")
-SOURCES = ["api.cpp", "cache.hip", "decode.hip", "prefill.hip", "blocks.hip"]
+SOURCES = ["api.cpp", "noalloc.cpp", "cache.hip", "decode.hip", "prefill.hip", "blocks.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled for all device code (hipcc -O3 would otherwise form them

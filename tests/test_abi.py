@@ -24,7 +24,7 @@ def _declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = pkv.load_library()
     syms = _declared_symbols()
-    assert len(syms) == 18, syms
+    assert len(syms) == 19, syms
     for s in syms:
         assert hasattr(lib, s), f"{s} missing from libpkv.so"
     assert set(syms) == set(pkv._SIGNATURES), "binding and header disagree"
@@ -184,3 +184,20 @@ def test_decode_plan_uses_the_real_maximum():
     assert pkv.decode_plan([], 32, 8, 128) == (0, 0, 0)
     with pytest.raises(pkv.PkvError):
         pkv.decode_plan([5, -1], 32, 8, 128)
+
+
+def test_noalloc_decode_rejects_before_launch():
+    """Partials beyond the library's 64 MiB array, and bad arguments, are reported before any launch
+    (no device is touched: the pointers here are never dereferenced)."""
+    lib = pkv.load_library()
+    nul = None
+    fake = ctypes.c_void_p(1 << 20)
+    args = [fake] * 6 + [nul]
+    # 64 x 64 heads x 256 partitions x 256 floats = 1 GiB of partials
+    assert lib.pkv_decode_workspace_bytes(64, 64, 8, 256, 131072, 512) > (64 << 20)
+    assert lib.pkv_paged_attn_decode_noalloc(*args, 64, 64, 8, 256, 16, 8, 8192, 131072, 1.0, 512, nul) \
+        == pkv.E_WORKSPACE_TOO_SMALL
+    assert lib.pkv_paged_attn_decode_noalloc(*args, 2, 5, 2, 128, 16, 8, 8, 100, 1.0, -1, nul) \
+        == pkv.E_INVALID_ARGUMENT
+    assert lib.pkv_paged_attn_decode_noalloc(*args, 2, 4, 2, 128, 16, 8, 8, 100, 1.0, -2, nul) \
+        == pkv.E_INVALID_ARGUMENT
