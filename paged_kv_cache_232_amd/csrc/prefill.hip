@@ -138,20 +138,23 @@ __device__ __forceinline__ bool resolve_tile(int y, const TileOrder& order,
                                              const int32_t* __restrict__ kv_indptr,
                                              const int32_t* __restrict__ kv_lens, int batch,
                                              int total_q, int total_kv, int kv_cap, TileWork& t) {
-  const uint32_t sched = order_dev != nullptr ? order_dev[y] : order.e[min(y, kMaxOrder - 1)];
+  // made explicitly wave-uniform: the request's extents then stay scalar, and so do the block-table
+  // reads the tile loads address from (a vector table read would wait for every load in flight)
+  const uint32_t sched = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(order_dev != nullptr ? order_dev[y] : order.e[min(y, kMaxOrder - 1)]));
   if (sched == kNoTile) return false;
   t.b = (int)(sched >> 16);
   t.qt = (int)(sched & 0xffffu);
   if (t.b >= batch) return false;
-  t.q0 = clampi(qo_indptr[t.b], 0, total_q);
-  t.qo = clampi(qo_indptr[t.b + 1], t.q0, total_q) - t.q0;
+  t.q0 = __builtin_amdgcn_readfirstlane(clampi(qo_indptr[t.b], 0, total_q));
+  t.qo = __builtin_amdgcn_readfirstlane(clampi(qo_indptr[t.b + 1], t.q0, total_q) - t.q0);
   if constexpr (PAGED) {
     t.kv0 = 0;
-    t.kv = clampi(kv_lens[t.b], 0, kv_cap);
+    t.kv = __builtin_amdgcn_readfirstlane(clampi(kv_lens[t.b], 0, kv_cap));
   } else {
-    const int k0 = clampi(kv_indptr[t.b], 0, total_kv);
+    const int k0 = __builtin_amdgcn_readfirstlane(clampi(kv_indptr[t.b], 0, total_kv));
     t.kv0 = k0;
-    t.kv = clampi(kv_indptr[t.b + 1], k0, total_kv) - k0;
+    t.kv = __builtin_amdgcn_readfirstlane(clampi(kv_indptr[t.b + 1], k0, total_kv) - k0);
   }
   return t.qt < (t.qo + BM - 1) / BM;
 }
@@ -328,8 +331,9 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     load_tile(v, 0, v_lds_of(0));
     if (n_kt > 1) load_tile(k, 1, k_lds_of(1));
   }
-  // last key any row of this wave can see (causal): tiles past it are skipped by the wave
-  const int wave_last_key = causal ? m0 + w * 32 + 31 + off : 0x7fffffff;
+  // last key any row of this wave can see (causal): tiles past it are skipped by the wave; a wave
+  // whose rows all lie past the request's end (the q tile's padding) skips every tile
+  const int wave_last_key = m0 + w * 32 >= qo ? -1 : (causal ? m0 + w * 32 + 31 + off : 0x7fffffff);
   int ks_slot = 0;  // t % 3
   for (int t = 0; t < n_kt; ++t) {
     const int n0 = t * C::BN;
@@ -602,7 +606,10 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if constexpr (C::PF > 1) fetch(2 * C::BN, S0{});
   }
   const int wave_first_row = m0 + w * 16;
-  const int wave_last_key = causal ? wave_first_row + 15 + off : 0x7fffffff;
+  // tiles past the last key a row of this wave sees are skipped, all of them by a wave whose rows
+  // lie past the request's end (the q tile's padding)
+  const int wave_last_key =
+      wave_first_row >= qo ? -1 : (causal ? wave_first_row + 15 + off : 0x7fffffff);
   auto step = [&](int t, auto slot_c) {
     const int n0 = t * C::BN;
     __syncthreads();  // tile t staged by every wave; tile t-1's buffer no longer read
