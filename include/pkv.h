@@ -116,6 +116,53 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           size_t workspace_bytes, void* stream);
 
 /*
+ * Measured decode planning. The libmir-cuda page does not fix its decode launch by rule alone:
+ * PagedAttentionBf16::new plans direct vs split decode and keeps the profiling state
+ * (profile_allowed, tuning_complete) of a CUDA autotuner so the choice is timed on the device.
+ * pkv_decode_tune times, on the caller's own buffers and stream, the library's default choice,
+ * the direct path, and split-KV with partitions of 256 / 512 / 1024 / 2048 tokens streamed 1, 2,
+ * 4, 8 or 16 to a wave (those whose partials fit the LDS budget and the given workspace), each
+ * the median of `repeats` launches after one untimed launch, and writes the fastest into *plan.
+ * The default choice is a candidate, so the plan is never slower than it on that measurement.
+ *   workspace      as for pkv_paged_attn_decode; split candidates needing more are skipped.
+ *                  pkv_decode_workspace_bytes(batch, ..., max_seq_len, 256) covers all of them.
+ *   out            is overwritten by every candidate (the result of any of them).
+ * The call synchronises with `stream` (HIP events): never call it while a stream is captured.
+ * A plan belongs to its shape bucket (batch, heads, head_dim, max_seq_len); the caller keeps it.
+ * Returns the status of the first failing launch, PKV_E_INVALID_ARGUMENT (null plan, repeats
+ * outside 1..1000), or PKV_E_HIP if the timing itself fails.
+ */
+typedef struct pkv_decode_tuned_plan {
+  int32_t partition_tokens;    /* 0: direct; > 0: split-KV with this many tokens per partition */
+  int32_t partitions_per_wave; /* split: consecutive partitions one wave streams (0: library's) */
+  int32_t max_seq_len;         /* the length bound the plan was measured for */
+  int32_t candidates;          /* configurations timed */
+  size_t workspace_bytes;      /* workspace pkv_paged_attn_decode_tuned needs with this plan */
+  float measured_us;           /* median time of the chosen configuration */
+  float default_us;            /* median time of the library's default choice */
+} pkv_decode_tuned_plan;
+
+int pkv_decode_tune(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                    int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                    int32_t repeats, void* stream, pkv_decode_tuned_plan* plan);
+
+/* paged_attn_decode with a measured plan: as pkv_paged_attn_decode (same arguments and result),
+ * with the plan's path, partition size and partitions per wave instead of partition_tokens.
+ * workspace must hold pkv_decode_workspace_bytes(..., plan->partition_tokens) bytes. Captures
+ * like pkv_paged_attn_decode (no allocation, no synchronisation). */
+int pkv_paged_attn_decode_tuned(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                                float* lse, int32_t batch, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, int32_t max_blocks_per_seq,
+                                int32_t max_seq_len, float scale,
+                                const pkv_decode_tuned_plan* plan, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * paged_attn_decode without a workspace, for callers that cannot allocate (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation). Same arguments, paths and
  * results as pkv_paged_attn_decode, less workspace / workspace_bytes: the split-KV partials live

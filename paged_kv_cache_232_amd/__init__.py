@@ -28,6 +28,20 @@ _c_f32 = ctypes.c_float
 _c_size = ctypes.c_size_t
 _c_i64 = ctypes.c_int64
 
+class DecodePlan(ctypes.Structure):
+    """pkv_decode_tuned_plan: a measured decode configuration for one shape bucket (caller-owned)."""
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("partitions_per_wave", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("candidates", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t), ("measured_us", ctypes.c_float),
+                ("default_us", ctypes.c_float)]
+
+    def __repr__(self):
+        return (f"DecodePlan(partition_tokens={self.partition_tokens}, partitions_per_wave="
+                f"{self.partitions_per_wave}, max_seq_len={self.max_seq_len}, candidates={self.candidates}, "
+                f"workspace_bytes={self.workspace_bytes}, measured_us={self.measured_us:.1f}, "
+                f"default_us={self.default_us:.1f})")
+
+
 # name -> (restype, argtypes)
 _SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -37,6 +51,13 @@ _SIGNATURES = {
     "pkv_paged_attn_decode": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                              _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                              _c_i32, _c_f32, _c_i32, _c_ptr, _c_size, _c_ptr]),
+    "pkv_decode_tune": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
+                                       _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_ptr, _c_size, _c_i32,
+                                       _c_ptr, ctypes.POINTER(DecodePlan)]),
+    "pkv_paged_attn_decode_tuned": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                                   _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                   _c_i32, _c_f32, ctypes.POINTER(DecodePlan), _c_ptr, _c_size,
+                                                   _c_ptr]),
     "pkv_paged_attn_decode_noalloc": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                                      _c_i32, _c_f32, _c_i32, _c_ptr]),
@@ -180,11 +201,13 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       max_seq_len: Optional[int] = None, partition_tokens: int = -1,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, k_scale: Optional[float] = None,
-                      v_scale: Optional[float] = None, window: int = 0) -> torch.Tensor:
+                      v_scale: Optional[float] = None, window: int = 0,
+                      plan: Optional[DecodePlan] = None) -> torch.Tensor:
     """Decode attention. q [B, Hq, D], caches [NB, Hkv, BS, D], block_tables [B, max_blocks] int32,
     seq_lens [B] int32. partition_tokens: 0 direct, > 0 split, -1 library choice. ``max_seq_len`` is a
     host hint (>= every seq_len); when omitted it is read from seq_lens (a device sync).
-    bf16 caches, or uint8 caches of fp8 (e4m3) codes with k_scale / v_scale (pkv_paged_attn_decode_fp8)."""
+    bf16 caches, or uint8 caches of fp8 (e4m3) codes with k_scale / v_scale (pkv_paged_attn_decode_fp8).
+    ``plan``: a DecodePlan from decode_tune (pkv_paged_attn_decode_tuned; bf16 caches, no window)."""
     lib = load_library()
     dev = q.device
     _need(q, "q", torch.bfloat16, 3, dev)
@@ -208,9 +231,20 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _need_out(out, "out", torch.bfloat16, (B, Hq, D), dev)
     if lse is not None:
         _need_out(lse, "lse", torch.float32, (B, Hq), dev)
+    if plan is not None:
+        if fp8 or window:
+            raise ValueError("a tuned plan runs bf16 caches without a window")
+        partition_tokens = plan.partition_tokens
     need = decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len, partition_tokens) if B else 0
     workspace = _need_workspace(workspace, need, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if plan is not None:
+        _check(lib.pkv_paged_attn_decode_tuned(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                               _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, D, BS, NB,
+                                               block_tables.shape[1], int(max_seq_len), float(scale),
+                                               ctypes.byref(plan), _ptr(workspace), wbytes, _stream(q)),
+               "paged_attn_decode_tuned")
+        return out
     if window:
         if fp8:
             raise ValueError("a sliding window is supported on bf16 caches")
@@ -261,6 +295,38 @@ def paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: t
                                              block_tables.shape[1], int(max_seq_len), float(scale),
                                              int(partition_tokens), _stream(q)), "paged_attn_decode_noalloc")
     return out
+
+
+def decode_tune(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                seq_lens: torch.Tensor, scale: float, *, max_seq_len: Optional[int] = None, repeats: int = 5,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> DecodePlan:
+    """Time the decode candidates on these buffers (pkv_decode_tune) and return the fastest as a
+    DecodePlan. Synchronises the current stream; not for use under graph capture. bf16 caches."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, 3, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    NB, Hkv, BS, D2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or D2 != D or block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("decode shapes disagree")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_out(out, "out", torch.bfloat16, (B, Hq, D), dev)
+    need = max(decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len, pt) for pt in (256, -1)) if B else 0
+    workspace = _need_workspace(workspace, need, dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    plan = DecodePlan()
+    _check(lib.pkv_decode_tune(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), _ptr(out),
+                               B, Hq, Hkv, D, BS, NB, block_tables.shape[1], int(max_seq_len), float(scale),
+                               _ptr(workspace), wbytes, int(repeats), _stream(q), ctypes.byref(plan)), "decode_tune")
+    return plan
 
 
 def reshape_and_cache_fp8(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

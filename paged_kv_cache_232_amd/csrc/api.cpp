@@ -4,6 +4,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "../../include/pkv.h"
 #include "api_internal.h"
 #include "kernels.h"
@@ -107,7 +110,7 @@ int pkv::decode_checked(const void* q, const void* k_cache, const void* v_cache,
                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                         int32_t max_seq_len, float scale, int32_t partition_tokens, void* workspace,
                         size_t workspace_bytes, int kv_fp8, float k_scale, float v_scale,
-                        int window, void* stream) {
+                        int window, int ppw_override, void* stream) {
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_seq_len < 0 || partition_tokens < -1)
     return PKV_E_INVALID_ARGUMENT;
@@ -144,6 +147,7 @@ int pkv::decode_checked(const void* q, const void* k_cache, const void* v_cache,
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.window = window;
+  a.ppw_override = ppw_override;
   a.partition_tokens =
       resolve_partition(batch, num_q_heads, num_kv_heads, max_seq_len, partition_tokens);
   if (a.partition_tokens > 0) {
@@ -174,7 +178,7 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
   return pkv::decode_checked(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                      max_seq_len, scale, partition_tokens, workspace, workspace_bytes, 0, 1.f, 1.f,
-                     0, stream);
+                     0, 0, stream);
 }
 
 int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -188,7 +192,7 @@ int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_
   return pkv::decode_checked(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                      max_seq_len, scale, partition_tokens, workspace, workspace_bytes, 1, k_scale,
-                     v_scale, 0, stream);
+                     v_scale, 0, 0, stream);
 }
 
 int pkv_paged_attn_decode_window(const void* q, const void* k_cache, const void* v_cache,
@@ -203,7 +207,7 @@ int pkv_paged_attn_decode_window(const void* q, const void* k_cache, const void*
   return pkv::decode_checked(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                      max_seq_len, scale, partition_tokens, workspace, workspace_bytes, 0, 1.f, 1.f,
-                     window, stream);
+                     window, 0, stream);
 }
 
 static pkv::DecodeWorkspaceLayout stream_state_layout(int batch, int num_q_heads, int head_dim) {
@@ -472,6 +476,114 @@ int pkv_validate_block_tables_h(const int32_t* block_tables_h, const int32_t* se
       if (row[j] < 0 || row[j] >= num_blocks) return PKV_E_BAD_TABLE;
   }
   return PKV_OK;
+}
+
+// Decode autotuning: every candidate configuration is launched on the caller's buffers and timed
+// with HIP events on the caller's stream; the fastest one is kept in the caller's plan.
+static const int32_t kTunePartitions[] = {256, 512, 1024, 2048};
+static const int32_t kTunePpw[] = {1, 2, 4, 8, 16};
+
+int pkv_decode_tune(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                    int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                    int32_t repeats, void* stream, pkv_decode_tuned_plan* plan) {
+  if (!plan || repeats < 1 || repeats > 1000) return PKV_E_INVALID_ARGUMENT;
+  // the library's own choice: also validates every argument before anything is timed
+  auto run = [&](int32_t pt, int32_t ppw) {
+    return pkv::decode_checked(q, k_cache, v_cache, block_tables, seq_lens, out, nullptr, batch,
+                               num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                               max_blocks_per_seq, max_seq_len, scale, pt, workspace,
+                               workspace_bytes, 0, 1.f, 1.f, 0, ppw, stream);
+  };
+  int st = run(-1, 0);
+  if (st != PKV_OK) return st;
+  if (batch == 0) {
+    memset(plan, 0, sizeof(*plan));
+    plan->max_seq_len = max_seq_len;
+    return PKV_OK;
+  }
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess) return PKV_E_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return PKV_E_HIP;
+  }
+  const hipStream_t s = (hipStream_t)stream;
+  std::vector<float> ts;
+  // median over `repeats` timed launches after one untimed launch; < 0 on a failed launch
+  auto time_us = [&](int32_t pt, int32_t ppw) -> float {
+    if (run(pt, ppw) != PKV_OK) return -1.f;
+    ts.clear();
+    for (int r = 0; r < repeats; ++r) {
+      if (hipEventRecord(e0, s) != hipSuccess) return -1.f;
+      if (run(pt, ppw) != PKV_OK) return -1.f;
+      float ms = 0.f;
+      if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+          hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
+        return -1.f;
+      ts.push_back(ms * 1000.f);
+    }
+    std::sort(ts.begin(), ts.end());
+    return ts[ts.size() / 2];
+  };
+  const int32_t def_pt = resolve_partition(batch, num_q_heads, num_kv_heads, max_seq_len, -1);
+  float best = time_us(-1, 0);
+  int32_t best_pt = def_pt, best_ppw = 0, n = 1;
+  const float def_us = best;
+  if (best >= 0.f) {
+    auto consider = [&](int32_t pt, int32_t ppw) {
+      const float us = time_us(pt, ppw);
+      ++n;
+      if (us >= 0.f && us < best) {
+        best = us;
+        best_pt = pt;
+        best_ppw = ppw;
+      }
+    };
+    consider(0, 0);
+    const int cap = pkv::decode_max_ppw(num_q_heads, num_kv_heads, head_dim);
+    for (int32_t pt : kTunePartitions) {
+      if (pt >= max_seq_len) continue;  // one partition: the direct path does the same work
+      const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                     max_seq_len, pt);
+      if (workspace == nullptr || need > workspace_bytes) continue;
+      const int32_t parts = (max_seq_len + pt - 1) / pt;
+      for (int32_t ppw : kTunePpw)
+        if (ppw <= cap && ppw <= parts) consider(pt, ppw);
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (best < 0.f) return PKV_E_HIP;
+  plan->partition_tokens = best_pt;
+  plan->partitions_per_wave = best_pt > 0 ? best_ppw : 0;
+  plan->max_seq_len = max_seq_len;
+  plan->candidates = n;
+  plan->workspace_bytes = pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                     max_seq_len, best_pt);
+  plan->measured_us = best;
+  plan->default_us = def_us;
+  return PKV_OK;
+}
+
+int pkv_paged_attn_decode_tuned(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                                float* lse, int32_t batch, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, int32_t max_blocks_per_seq,
+                                int32_t max_seq_len, float scale,
+                                const pkv_decode_tuned_plan* plan, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!plan || plan->partition_tokens < 0 || plan->partitions_per_wave < 0 ||
+      plan->partitions_per_wave > 16)
+    return PKV_E_INVALID_ARGUMENT;
+  return pkv::decode_checked(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch,
+                             num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             max_blocks_per_seq, max_seq_len, scale, plan->partition_tokens,
+                             workspace, workspace_bytes, 0, 1.f, 1.f, 0,
+                             plan->partition_tokens > 0 ? plan->partitions_per_wave : 0, stream);
 }
 
 int pkv_copy_blocks(const uint64_t* k_cache_ptrs, const uint64_t* v_cache_ptrs, int32_t num_layers,

@@ -11,9 +11,9 @@
 //     split-KV: one single-wave work-group per partition; direct: 4 waves per sequence take
 //     chunks round robin and are combined through LDS at the end;
 //   * QK^T on a 16x16x32 bf16 MFMA with the K half page as the A operand (rows = 16 tokens) and
-//     the GQA group's q rows as B (16 columns); a bf16 K half page is read in contiguous 1 KiB
-//     wave loads and staged through the wave's LDS tile (which V then reuses), an fp8 one is
-//     loaded straight into the operand layout in 8-byte pieces;
+//     the GQA group's q rows as B (16 columns); a K half page is read in contiguous wave loads
+//     (1 KiB of bf16, 512 bytes of fp8 codes) and staged through the wave's LDS tile (which V
+//     then reuses), fp8 codes converted to bf16 as they are read back;
 //   * the score tile lands in the layout the PV MFMA needs for its B operand: each lane already
 //     holds 8 probabilities of one head, so P never moves between lanes;
 //   * V is read from HBM in contiguous 1 KiB wave loads, staged row-major in a per-wave LDS tile
@@ -40,6 +40,8 @@ constexpr float kRescaleLog2 = 8.0f;  // raise a running max only when exceeded 
 constexpr int kPrefetch = 2;          // 32-token chunks per wave in flight (loads issued ahead)
 constexpr int kMergeUnroll = 8;       // merge: partial rows per thread in flight
 constexpr int kMaxStageBytes = 68 * 1024;  // split: LDS for parked partials per wave
+// fp8 caches: most consecutive partitions one split wave streams (4 and 16 measured slower)
+constexpr int kFp8MaxPpw = 2;
 
 template <int D>
 struct DecodeCfg {
@@ -48,6 +50,7 @@ struct DecodeCfg {
   static constexpr int VU = D / 32;           // 16-byte V units per lane per half page
   static constexpr int RS = 2 * D + 32;       // LDS bytes per staged V row (pad: conflict-free tr reads)
   static constexpr int RSK = 2 * D + 16;      // LDS bytes per staged K row (pad: conflict-free reads)
+  static constexpr int RSK8 = D + 8;          // the same for a row of fp8 K codes
   static constexpr int WAVE_LDS = 32 * RS;    // one wave's 32-row V tile
   static_assert(WAVE_LDS >= D * 16 * 4, "combine buffer must fit in a wave's V tile");
 };
@@ -64,14 +67,9 @@ struct DecodeChunk {
 // 8 elements of a chunk piece as bf16 (fp8 e4m3 codes convert exactly)
 __device__ __forceinline__ u32x4 piece_bf16(u32x4 x) { return x; }
 __device__ __forceinline__ u32x4 piece_bf16(u32x2 x) { return fp8x8_to_bf16x8(x); }
-__device__ __forceinline__ u32x4 load_piece(const uint16_t* p, u32x4*) { return load16(p); }
-__device__ __forceinline__ u32x2 load_piece(const uint8_t* p, u32x2*) { return load8(p); }
-// Non-temporal loads for pieces whose load instruction reads whole 128-byte lines that nothing
-// reads again: V always (a contiguous 1 KiB, or 512 bytes of fp8 codes, per wave), and K of a
-// bf16 cache, which is read the same way and staged through LDS. Keeping these lines out of the
-// caches' normal replacement measured 8-15 % faster on the decode workloads. fp8 K is loaded
-// straight in the MFMA operand layout, where an instruction reads only part of each line (the
-// next instructions read the rest); it keeps the default policy, which measured faster there.
+// Non-temporal loads: every K and V load instruction reads whole 128-byte lines (a contiguous
+// 1 KiB of bf16, or 512 bytes of fp8 codes, per wave) that nothing reads again. Keeping these
+// lines out of the caches' normal replacement measured 8-15 % faster on the decode workloads.
 __device__ __forceinline__ u32x4 load_piece_nt(const uint16_t* p, u32x4*) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -185,7 +183,6 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
   TableWindow tw;
   tw.init(trow, max_blocks, (t_begin + w * 32) >> bs_shift, lane);
 
-  const int koff = col * D + 8 * qg;  // this lane's K element within a 16-row half page
   const int voff = lane * 8;          // this lane's first V element within a half page
 
   auto load = [&](Chunk& ch, int c) {
@@ -201,9 +198,9 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
       const KVT* vp = vc + base;
 #pragma unroll
       for (int i = 0; i < C::KK; ++i) {
-        // bf16: whole 1 KiB rows like V (staged through LDS below); fp8: the MFMA operand pieces
-        if constexpr (FP8) ch.k[hh][i] = load_piece(kp + koff + i * 32, (Piece*)nullptr);
-        else ch.k[hh][i] = load_piece_nt(kp + voff + i * 512, (Piece*)nullptr);
+        // whole rows like V, contiguous per instruction (1 KiB bf16, 512 bytes fp8), staged
+        // through LDS below
+        ch.k[hh][i] = load_piece_nt(kp + voff + i * 512, (Piece*)nullptr);
       }
 #pragma unroll
       for (int i = 0; i < C::VU; ++i) ch.v[hh][i] = load_piece_nt(vp + voff + i * 512, (Piece*)nullptr);
@@ -217,13 +214,27 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
     // S^T[token][head] for the two half pages
     f32x4 s[2];
     if constexpr (FP8) {
+      // fp8 K rows staged in the wave's LDS tile (row stride RSK8 bytes), read back as 8-code
+      // operand pieces and converted to bf16; the V rows then overwrite the tile
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < C::KK; ++i) {
+          const int u = i * 64 + lane;
+          const int row = u / (D / 8);
+          *reinterpret_cast<u32x2*>(vbuf + (16 * hh + row) * C::RSK8 + (u - row * (D / 8)) * 8) = ch.k[hh][i];
+        }
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk)
-          s[hh] = mfma16(as_bf16x8(piece_bf16(ch.k[hh][kk])), qreg[kk], s[hh]);
+          s[hh] = mfma16(as_bf16x8(fp8x8_to_bf16x8(*reinterpret_cast<const u32x2*>(
+                             vbuf + (16 * hh + col) * C::RSK8 + 32 * kk + 8 * qg))),
+                         qreg[kk], s[hh]);
       }
+      __builtin_amdgcn_wave_barrier();
     } else {
       // K rows staged in the wave's LDS tile (row stride RSK), read back as the A operand; the V
       // rows then overwrite the tile (LDS operations of one wave run in order)
@@ -337,29 +348,30 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
     }
   };
 
-  // chunks w, w+NW, ... with the next kPrefetch-1 chunks' loads in flight while one is processed.
+  // chunks w, w+NW, ... with the next PF-1 chunks' loads in flight while one is processed.
   // The steady-state loop issues its look-ahead loads unconditionally, so the compiler can count
   // exactly which loads a chunk must wait for; the tail drains in a guarded epilogue.
   {
-    Chunk ring[kPrefetch];
+    constexpr int PF = kPrefetch;
+    Chunk ring[PF];
     int c = w;
 #pragma unroll
-    for (int i = 0; i < kPrefetch - 1; ++i)
+    for (int i = 0; i < PF - 1; ++i)
       if (c + i * NW < n_chunks) load(ring[i], c + i * NW);
-    while (c + (2 * kPrefetch - 2) * NW < n_chunks) {
+    while (c + (2 * PF - 2) * NW < n_chunks) {
 #pragma unroll
-      for (int sl = 0; sl < kPrefetch; ++sl) {
-        load(ring[(sl + kPrefetch - 1) % kPrefetch], c + (kPrefetch - 1) * NW);
+      for (int sl = 0; sl < PF; ++sl) {
+        load(ring[(sl + PF - 1) % PF], c + (PF - 1) * NW);
         process(ring[sl], c);
         c += NW;
       }
     }
 #pragma unroll
-    for (int sl = 0; sl < 2 * kPrefetch - 1; ++sl) {
+    for (int sl = 0; sl < 2 * PF - 1; ++sl) {
       if (c < n_chunks) {
-        const int ahead = c + (kPrefetch - 1) * NW;
-        if (ahead < n_chunks) load(ring[(sl + kPrefetch - 1) % kPrefetch], ahead);
-        process(ring[sl % kPrefetch], c);
+        const int ahead = c + (PF - 1) * NW;
+        if (ahead < n_chunks) load(ring[(sl + PF - 1) % PF], ahead);
+        process(ring[sl % PF], c);
         c += NW;
       }
     }
@@ -602,6 +614,12 @@ decode_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ 
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int decode_max_ppw(int num_q_heads, int num_kv_heads, int head_dim) {
+  const int G = num_q_heads / num_kv_heads;
+  const int slot_bytes = (std::min(16, G) * (head_dim + 4) + 32) * (int)sizeof(float);
+  return std::min(16, 1 + kMaxStageBytes / slot_bytes);
+}
+
 DecodeWorkspaceLayout decode_workspace_layout(int batch, int num_q_heads, int head_dim,
                                               int max_seq_len, int partition_tokens) {
   DecodeWorkspaceLayout w{0, 0, 0, 0, 0};
@@ -634,15 +652,17 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     // faster), parking all but the last partial in LDS; the largest count that the LDS budget
     // allows and that still leaves 512 waves (two per CU) is taken.
     const int slot_bytes = (std::min(16, G) * (D + 4) + 32) * (int)sizeof(float);
+    const int lds_cap = decode_max_ppw(a.num_q_heads, a.num_kv_heads, D);
     // Partitions holding visible keys: with a sliding window only the last ones. The fp8 cache
     // streams at most two partitions per wave (measured fastest there: four or more were slower).
     int p_act = a.max_partitions;
     if (a.window > 0) p_act = std::min(p_act, (a.window + 31) / a.partition_tokens + 2);
     int ppw = 1;
-    if (p_act >= 64) {
+    if (a.ppw_override > 0) {
+      ppw = std::min(a.ppw_override, lds_cap);
+    } else if (p_act >= 64) {
       const long units = (long)a.batch * a.num_kv_heads * n_hg;
-      const int lds_cap = 1 + kMaxStageBytes / slot_bytes;
-      for (int c = FP8 ? 2 : 16; c > 1; c /= 2)
+      for (int c = FP8 ? kFp8MaxPpw : 16; c > 1; c /= 2)
         if (c <= lds_cap && units * ((p_act + c - 1) / c) >= 512) {
           ppw = c;
           break;

@@ -28,6 +28,7 @@ struct DecodeArgs {
   int kv_fp8;            // caches hold fp8 (e4m3) codes dequantised by k_scale / v_scale
   float k_scale, v_scale;
   int window;            // > 0: keys [L - window, L) only
+  int ppw_override;      // split: consecutive partitions per wave (0 = the library's choice)
   // split workspace (null for direct)
   float* o_part;
   float* m_part;
@@ -50,6 +51,9 @@ DecodeWorkspaceLayout decode_workspace_layout(int batch, int num_q_heads, int he
                                               int max_seq_len, int partition_tokens);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Most consecutive split partitions one wave can stream (its finished partials wait in LDS).
+int decode_max_ppw(int num_q_heads, int num_kv_heads, int head_dim);
 
 struct PrefillArgs {
   const void* q;

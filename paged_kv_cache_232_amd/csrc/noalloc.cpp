@@ -69,5 +69,5 @@ extern "C" int pkv_paged_attn_decode_noalloc(
   return pkv::decode_checked(q, k_cache, v_cache, block_tables, seq_lens, out, lse, batch,
                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                              max_blocks_per_seq, max_seq_len, scale, partition_tokens, ws,
-                             need > 0 ? kScratchBytes : 0, 0, 1.f, 1.f, 0, stream);
+                             need > 0 ? kScratchBytes : 0, 0, 1.f, 1.f, 0, 0, stream);
 }

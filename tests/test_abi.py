@@ -24,7 +24,7 @@ def _declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = pkv.load_library()
     syms = _declared_symbols()
-    assert len(syms) == 19, syms
+    assert len(syms) == 21, syms
     for s in syms:
         assert hasattr(lib, s), f"{s} missing from libpkv.so"
     assert set(syms) == set(pkv._SIGNATURES), "binding and header disagree"
@@ -201,3 +201,27 @@ def test_noalloc_decode_rejects_before_launch():
         == pkv.E_INVALID_ARGUMENT
     assert lib.pkv_paged_attn_decode_noalloc(*args, 2, 4, 2, 128, 16, 8, 8, 100, 1.0, -2, nul) \
         == pkv.E_INVALID_ARGUMENT
+
+
+def test_decode_tune_argument_errors():
+    """The tuner and the planned call check their arguments before launching anything."""
+    lib = pkv.load_library()
+    nul = None
+    fake = ctypes.c_void_p(1 << 20)
+    plan = pkv.DecodePlan()
+    args = [fake] * 6
+    # no plan / bad repeats / unsupported head_dim: rejected before any launch
+    assert lib.pkv_decode_tune(*args, 2, 8, 2, 128, 16, 64, 8, 100, 1.0, nul, 0, 5, nul, nul) == pkv.E_INVALID_ARGUMENT
+    assert lib.pkv_decode_tune(*args, 2, 8, 2, 128, 16, 64, 8, 100, 1.0, nul, 0, 0, nul, ctypes.byref(plan)) \
+        == pkv.E_INVALID_ARGUMENT
+    assert lib.pkv_decode_tune(*args, 2, 8, 2, 96, 16, 64, 8, 100, 1.0, nul, 0, 5, nul, ctypes.byref(plan)) \
+        == pkv.E_UNSUPPORTED
+    targs = [fake] * 6 + [nul]
+    assert lib.pkv_paged_attn_decode_tuned(*targs, 2, 8, 2, 128, 16, 64, 8, 100, 1.0, nul, nul, 0, nul) \
+        == pkv.E_INVALID_ARGUMENT
+    bad = pkv.DecodePlan(partition_tokens=512, partitions_per_wave=17)
+    assert lib.pkv_paged_attn_decode_tuned(*targs, 2, 8, 2, 128, 16, 64, 8, 1000, 1.0, ctypes.byref(bad), nul, 0,
+                                           nul) == pkv.E_INVALID_ARGUMENT
+    ok = pkv.DecodePlan(partition_tokens=512, partitions_per_wave=2)
+    assert lib.pkv_paged_attn_decode_tuned(*targs, 2, 8, 2, 128, 16, 64, 8, 1000, 1.0, ctypes.byref(ok), nul, 0,
+                                           nul) == pkv.E_WORKSPACE_TOO_SMALL
