@@ -15,6 +15,12 @@ over tiles of resident blocks, a small decode step (eager and replayed from a HI
 block-management calls (copy_blocks over 32 layers, swap_blocks to pinned host
 memory) are timed separately, outside the step.
 
+Besides rates and roofline fractions, every call reports tokens per second (decoded sequences and
+KV tokens attended for decode, query rows for prefill); the decode step is also timed host-inclusive
+(wall clock over back-to-back calls), eager and replayed from a graph; a plain 1 GiB device copy is
+timed for context; the batched and long-context decodes also run with a plan measured by
+pkv_decode_tune.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --calibrate-copy     (times a plain 1 GiB device copy, for counter scaling)
 """
@@ -121,8 +127,11 @@ def scatter_bytes(T, hkv, d) -> int:
 
 # ----------------------------------------------------------------------------------------------
 class Case:
-    def __init__(self, name, fn, kind, work, unit):
+    def __init__(self, name, fn, kind, work, unit, tokens=None):
         self.name, self.fn, self.kind, self.work, self.unit = name, fn, kind, work, unit
+        # tokens: {label: count} per call, reported as count / time (e.g. decoded sequences,
+        # KV tokens attended, prefill query rows)
+        self.tokens = tokens or {}
         self.ms = []
 
     def rate(self, ms):
@@ -145,12 +154,13 @@ def build_cases(dev):
     cases["scatter5"] = Case(
         "reshape_and_cache (chunked prefill, 16 req, hd 256)",
         lambda: pkv.reshape_and_cache(c5["k_new"], c5["v_new"], c5["kc"], c5["vc"], c5["slots"]),
-        "hbm", scatter_bytes(T5, spec["num_kv_heads"], spec["head_dim"]), "GB/s")
+        "hbm", scatter_bytes(T5, spec["num_kv_heads"], spec["head_dim"]), "GB/s", {"tokens_per_s": T5})
     cases["paged5"] = Case(
         "paged_prefill (16 req, prefix U[0,4096], chunk U[64,1024], 16/4 heads, hd 256)",
         lambda: pkv.paged_prefill(c5["q"], c5["kc"], c5["vc"], c5["bt"], c5["qi"], c5["kl"], True, c5["scale"],
                                   qo_indptr_h=c5["qi_h"], kv_lens_h=c5["kl_h"], out=c5["out"]),
-        "mfma", prefill_flops(chunk, kvl5, spec["num_q_heads"], spec["head_dim"], True), "TFLOP/s")
+        "mfma", prefill_flops(chunk, kvl5, spec["num_q_heads"], spec["head_dim"], True), "TFLOP/s",
+        {"q_tokens_per_s": T5})
     meta = {"T5": T5, "prefix_mean": float(ci.prefix_lens.float().mean()), "chunk_mean": T5 / len(chunk)}
     del ci
 
@@ -165,7 +175,8 @@ def build_cases(dev):
         "ragged_prefill (8 req, U[128,2048], 32/8 heads, hd 128, causal)",
         lambda: pkv.ragged_prefill(c2["q"], c2["k"], c2["v"], c2["qi"], c2["ki"], True, c2["scale"],
                                    qo_indptr_h=c2["qi_h"], kv_indptr_h=c2["ki_h"], out=c2["out"]),
-        "mfma", prefill_flops(lens2, lens2, spec["num_q_heads"], spec["head_dim"], True), "TFLOP/s")
+        "mfma", prefill_flops(lens2, lens2, spec["num_q_heads"], spec["head_dim"], True), "TFLOP/s",
+        {"q_tokens_per_s": sum(lens2)})
     meta["lens2"] = lens2
     del ri
 
@@ -188,13 +199,31 @@ def build_cases(dev):
             return lambda: pkv.paged_attn_decode(c["q"], c["kc"], c["vc"], c["bt"], c["sl"], c["scale"],
                                                  max_seq_len=c["msl"], partition_tokens=pt, out=c["out"],
                                                  workspace=c["ws"])
+        dtok = {"seqs_per_s": B, "kv_tokens_per_s": sum(lens)}
         cases[key] = Case(f"paged_attn_decode ({CONFIGS[cid]['name']}, B={B}, {Hq}/{Hkv} heads, hd {D})",
-                          mk(), "hbm", work, "GB/s")
+                          mk(), "hbm", work, "GB/s", dtok)
+        # the measured plan for this shape (pkv_decode_tune, once at set-up)
+        plan = pkv.decode_tune(c["q"], c["kc"], c["vc"], c["bt"], c["sl"], c["scale"], max_seq_len=c["msl"],
+                               repeats=5, out=c["out"])
+        c["plan"] = plan
+        c["ws_plan"] = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+
+        def mkp(c=c):
+            return lambda: pkv.paged_attn_decode(c["q"], c["kc"], c["vc"], c["bt"], c["sl"], c["scale"],
+                                                 max_seq_len=c["msl"], out=c["out"], workspace=c["ws_plan"],
+                                                 plan=c["plan"])
+        cases[key + "_tuned"] = Case(f"paged_attn_decode_tuned ({CONFIGS[cid]['name']}, plan: partition "
+                                     f"{plan.partition_tokens}, {plan.partitions_per_wave} per wave)",
+                                     mkp(), "hbm", work, "GB/s", dtok)
+        meta[f"plan{cid}"] = {"partition_tokens": plan.partition_tokens,
+                              "partitions_per_wave": plan.partitions_per_wave, "candidates": plan.candidates,
+                              "tune_measured_us": round(plan.measured_us, 1),
+                              "tune_default_us": round(plan.default_us, 1)}
         if cid == 3:
             cases["decode3_direct"] = Case("paged_attn_decode direct path (batched decode)", mk(c, 0), "hbm", work,
-                                           "GB/s")
+                                           "GB/s", dtok)
             cases["decode3_split"] = Case("paged_attn_decode split 512 (batched decode)", mk(c, 512), "hbm", work,
-                                          "GB/s")
+                                          "GB/s", dtok)
         if cid == 4:
             # sliding window of the last 8192 tokens over the long contexts (split 512)
             W = 8192
@@ -205,7 +234,8 @@ def build_cases(dev):
                                                      max_seq_len=c["msl"], partition_tokens=512, out=c["out"],
                                                      workspace=c["ws"], window=W)
             cases["decode4_window"] = Case(f"paged_attn_decode_window (long-context, window {W}, split 512)",
-                                           mkw(), "hbm", decode_bytes(wlens, Hq, Hkv, D, di.block_size), "GB/s")
+                                           mkw(), "hbm", decode_bytes(wlens, Hq, Hkv, D, di.block_size), "GB/s",
+                                           {"seqs_per_s": B, "kv_tokens_per_s": sum(wlens)})
         if cid == 3:
             # the batched workload streamed over tiles of 64 resident blocks (1024 tokens): one
             # launch per tile folded into a running state, then finalize
@@ -229,7 +259,7 @@ def build_cases(dev):
                     sdec.step(t_tab, t_len)
                 sdec.finalize(out=c["out"])
             cases["decode3_streamed"] = Case(f"streamed decode, batched workload over {ntile} tiles of {cap} blocks",
-                                             streamed, "hbm", work, "GB/s")
+                                             streamed, "hbm", work, "GB/s", dtok)
         # the same workload over an fp8 (e4m3) cache (timed alone): codes of cache / scale, one byte
         # per element, so half the bytes of the bf16 cache
         c["k_scale"], c["v_scale"] = 0.02, 0.02
@@ -241,7 +271,7 @@ def build_cases(dev):
                                                  max_seq_len=c["msl"], partition_tokens=pt, out=c["out"],
                                                  workspace=c["ws"], k_scale=c["k_scale"], v_scale=c["v_scale"])
         cases[key + "_fp8"] = Case(f"paged_attn_decode_fp8 ({CONFIGS[cid]['name']} over an e4m3 cache)", mk8(),
-                                   "hbm", decode_bytes_fp8(lens, Hq, Hkv, D, di.block_size), "GB/s")
+                                   "hbm", decode_bytes_fp8(lens, Hq, Hkv, D, di.block_size), "GB/s", dtok)
         meta[f"lens{cid}_sum"] = sum(lens)
         meta[f"flops{cid}"] = decode_flops(lens, Hq, D)
         del di
@@ -273,10 +303,11 @@ def build_cases(dev):
     with torch.cuda.graph(graph):
         small_step()
     sbytes = decode_bytes(cap, 32, 8, 128, 16) + scatter_bytes(8, 8, 128)
+    stok = {"seqs_per_s": 8, "kv_tokens_per_s": sum(cap)}
     cases["decode_step_eager"] = Case("decode step, eager launches (scatter + decode, B=8, U[512,2048])",
-                                      small_step, "hbm", sbytes, "GB/s")
+                                      small_step, "hbm", sbytes, "GB/s", stok)
     cases["decode_step_graph"] = Case("decode step replayed from a HIP graph (same step)", graph.replay, "hbm",
-                                      sbytes, "GB/s")
+                                      sbytes, "GB/s", stok)
     meta["graph"] = graph  # keep the captured graph alive
 
     # block management around the cache (timed alone, outside the step): copy_blocks over 32
@@ -302,8 +333,10 @@ def build_cases(dev):
 
 STEP = ["scatter5", "paged5", "ragged2", "decode3", "decode4"]
 # timed alone, outside the step
-EXTRA = ["decode3_direct", "decode3_split", "decode3_fp8", "decode4_fp8", "decode4_window", "decode3_streamed",
-         "decode_step_eager", "decode_step_graph", "copy_blocks", "swap_out"]
+EXTRA = ["decode3_direct", "decode3_split", "decode3_tuned", "decode4_tuned", "decode3_fp8", "decode4_fp8",
+         "decode4_window", "decode3_streamed", "decode_step_eager", "decode_step_graph", "copy_blocks", "swap_out"]
+# host-inclusive latency (wall clock over many back-to-back calls, then one synchronisation)
+HOST_TIMED = ["decode_step_eager", "decode_step_graph"]
 
 
 def time_step(cases, steps, warmup):
@@ -330,6 +363,19 @@ def time_step(cases, steps, warmup):
     for k in STEP:
         cases[k].ms = [a.elapsed_time(b) for a, b in ev[k]]
     return whole0.elapsed_time(whole1) / steps, wall
+
+
+def time_host(case, reps=200, warmup=20):
+    """Wall-clock microseconds per call, launch overhead included: reps calls back to back, then one
+    synchronisation (the host's view of a serving loop)."""
+    for _ in range(warmup):
+        case.fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        case.fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / reps * 1e6
 
 
 def time_alone(case, reps=20, warmup=5):
@@ -382,7 +428,9 @@ def cpu_baseline(meta):
                         "sample": f"ragged prefill workload, request {b} ({q1 - q0} rows) alone, {dt2:.2f} s"}}
 
 
-def calibrate_copy(dev):
+def copy_bandwidth(dev):
+    """A plain 1 GiB device-to-device copy (the runtime's), timed with HIP events: the practical
+    streaming rate of this machine, reported beside the nominal 8 TB/s."""
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -397,7 +445,13 @@ def calibrate_copy(dev):
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / 5
-    print(json.dumps({"copy_bytes_each_way": n, "ms": ms, "GB/s_read_plus_write": 2 * n / ms / 1e6}))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_bytes_each_way": n, "ms": round(ms, 4), "GB/s_read_plus_write": round(2 * n / ms / 1e6, 1)}
+
+
+def calibrate_copy(dev):
+    print(json.dumps(copy_bandwidth(dev)))
 
 
 def main():
@@ -428,6 +482,8 @@ def main():
     ms_step, wall = time_step(cases, args.steps, args.warmup)
     for k in EXTRA:
         time_alone(cases[k])
+    host_us = {k: time_host(cases[k]) for k in HOST_TIMED}
+    copy = copy_bandwidth(dev)
 
     def summary(k):
         c = cases[k]
@@ -435,9 +491,14 @@ def main():
         med = statistics.median(c.ms)
         peak = {"hbm": HBM_PEAK_GBS, "mfma": MFMA_BF16_PEAK_TFLOPS, "pcie": PCIE_PEAK_GBS}[c.kind]
         r = c.rate(avg)
-        return {"call": c.name, "avg_ms": round(avg, 5), "median_ms": round(med, 5), "work": c.work,
-                "rate": round(r, 2), "unit": c.unit, "frac_of_peak": round(r / peak, 4),
-                "hbm_traffic_bytes": measured_traffic(k)}
+        d = {"call": c.name, "avg_ms": round(avg, 5), "median_ms": round(med, 5), "work": c.work,
+             "rate": round(r, 2), "unit": c.unit, "frac_of_peak": round(r / peak, 4),
+             "hbm_traffic_bytes": measured_traffic(k)}
+        for label, count in c.tokens.items():
+            d[label] = round(count / (avg * 1e-3), 1)
+        if k in host_us:
+            d["host_inclusive_us"] = round(host_us[k], 2)
+        return d
 
     per = {k: summary(k) for k in STEP + EXTRA}
     dec_ms = sum(statistics.fmean(cases[k].ms) for k in ("decode3", "decode4"))
@@ -479,6 +540,12 @@ def main():
                      "achieved": round(dach, 2), "peak": dpeak,
                      "unit": "GB/s" if dc.kind == "hbm" else "TFLOP/s", "frac": round(dach / dpeak, 4),
                      "traffic": measured_traffic(dom)},
+        "tokens_per_s": {k: {t: v for t, v in per[k].items() if t.endswith("_per_s")} for k in STEP},
+        "copy_1gib": copy,
+        "decode_plans": {k: meta[k] for k in ("plan3", "plan4")},
+        "context": {"pages_engine_prefill_tok_s": 3880, "hardware": "NVIDIA GB10 (sm_121)",
+                    "note": "whole-engine prefill rate of an unnamed model quoted on the Atlas flashinfer page; "
+                            "not comparable with a single attention kernel, not a target"},
         "per_call": per,
         "wall_s_timed": round(wall, 4),
     }
