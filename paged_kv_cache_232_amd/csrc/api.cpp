@@ -21,8 +21,7 @@ bool block_size_ok(int bs) { return bs >= 16 && bs <= 256 && (bs & (bs - 1)) == 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_E_HIP; }
 
-// Prefill: q rows per work-group tile, and the most tiles one launch takes (one grid row each)
-constexpr int kPrefillTileRows = 128;
+// Prefill: the most (request, q tile) work items one launch takes (one grid row each)
 constexpr int64_t kMaxPrefillGridRows = 65528;
 
 // Auto choice of the decode path. A direct launch gives one work-group per (sequence, kv head,
@@ -314,7 +313,7 @@ int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void*
 static int check_prefill_common(const void* q, const void* out, const int32_t* qo_indptr,
                                 const int32_t* qo_indptr_h, int32_t batch, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim, int* max_qo, int* total_q,
-                                int64_t* tiles) {
+                                int64_t* tiles, int* tile_rows) {
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0) return PKV_E_INVALID_ARGUMENT;
   if (num_q_heads % num_kv_heads != 0) return PKV_E_INVALID_ARGUMENT;
   if (!head_dim_ok(head_dim)) return PKV_E_UNSUPPORTED;
@@ -323,6 +322,7 @@ static int check_prefill_common(const void* q, const void* out, const int32_t* q
   *max_qo = 0;
   *total_q = 0;
   *tiles = 0;
+  *tile_rows = pkv::prefill_tile_rows(head_dim);
   if (batch == 0) return PKV_OK;
   if (!qo_indptr_h || !qo_indptr) return PKV_E_INVALID_ARGUMENT;
   if (qo_indptr_h[0] != 0) return PKV_E_INVALID_ARGUMENT;
@@ -336,8 +336,8 @@ static int check_prefill_common(const void* q, const void* out, const int32_t* q
   *total_q = qo_indptr_h[batch];
   if (*total_q > 0 && (!q || !out)) return PKV_E_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(out)) return PKV_E_INVALID_ARGUMENT;
-  if (batch > 65535 || mx > 0xffff * kPrefillTileRows) return PKV_E_UNSUPPORTED;
-  *tiles = pkv::prefill_tile_count(batch, qo_indptr_h);
+  if (batch > 65535 || (int64_t)mx > 0xffffll * *tile_rows) return PKV_E_UNSUPPORTED;
+  *tiles = pkv::prefill_tile_count(batch, qo_indptr_h, *tile_rows);
   if (*tiles > kMaxPrefillGridRows) return PKV_E_UNSUPPORTED;
   return PKV_OK;
 }
@@ -352,12 +352,12 @@ static int check_prefill_workspace(int64_t tiles, const void* workspace, size_t 
 
 size_t pkv_prefill_workspace_bytes(int32_t batch, const int32_t* qo_indptr_h, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t head_dim) {
-  int max_qo = 0, total_q = 0;
+  int max_qo = 0, total_q = 0, tile_rows = 0;
   int64_t tiles = 0;
   // q / out are not needed to size the schedule: pass any aligned non-null stand-in
   static const int32_t stand_in[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
   if (check_prefill_common(stand_in, stand_in, stand_in, qo_indptr_h, batch, num_q_heads,
-                           num_kv_heads, head_dim, &max_qo, &total_q, &tiles) != PKV_OK)
+                           num_kv_heads, head_dim, &max_qo, &total_q, &tiles, &tile_rows) != PKV_OK)
     return 0;
   return pkv::prefill_workspace_bytes(tiles);
 }
@@ -367,10 +367,10 @@ int pkv_ragged_prefill(const void* q, const void* k, const void* v, void* out,
                        const int32_t* qo_indptr_h, const int32_t* kv_indptr_h, int32_t batch,
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t causal,
                        float scale, void* workspace, size_t workspace_bytes, void* stream) {
-  int max_qo = 0, total_q = 0;
+  int max_qo = 0, total_q = 0, tile_rows = 0;
   int64_t tiles = 0;
   int st = check_prefill_common(q, out, qo_indptr, qo_indptr_h, batch, num_q_heads, num_kv_heads,
-                                head_dim, &max_qo, &total_q, &tiles);
+                                head_dim, &max_qo, &total_q, &tiles, &tile_rows);
   if (st != PKV_OK || batch == 0) return st;
   if (!kv_indptr_h || !kv_indptr) return PKV_E_INVALID_ARGUMENT;
   if (kv_indptr_h[0] != 0) return PKV_E_INVALID_ARGUMENT;
@@ -400,6 +400,7 @@ int pkv_ragged_prefill(const void* q, const void* k, const void* v, void* out,
   a.max_qo_len = max_qo;
   a.total_q = total_q;
   a.total_kv = total_kv;
+  a.tile_rows = tile_rows;
   a.tiles = tiles;
   a.workspace = workspace;
   const hipError_t e = pkv::launch_ragged_prefill(a, (hipStream_t)stream);
@@ -413,10 +414,10 @@ int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                       int32_t num_blocks, int32_t max_blocks_per_seq, int32_t causal, float scale,
                       void* workspace, size_t workspace_bytes, void* stream) {
-  int max_qo = 0, total_q = 0;
+  int max_qo = 0, total_q = 0, tile_rows = 0;
   int64_t tiles = 0;
   int st = check_prefill_common(q, out, qo_indptr, qo_indptr_h, batch, num_q_heads, num_kv_heads,
-                                head_dim, &max_qo, &total_q, &tiles);
+                                head_dim, &max_qo, &total_q, &tiles, &tile_rows);
   if (st != PKV_OK || batch == 0) return st;
   if (!block_size_ok(block_size)) return PKV_E_UNSUPPORTED;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PKV_E_INVALID_ARGUMENT;
@@ -452,6 +453,7 @@ int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
   a.kv_lens_h = kv_lens_h;
   a.max_qo_len = max_qo;
   a.total_q = total_q;
+  a.tile_rows = tile_rows;
   a.tiles = tiles;
   a.workspace = workspace;
   const hipError_t e = pkv::launch_paged_prefill(a, (hipStream_t)stream);

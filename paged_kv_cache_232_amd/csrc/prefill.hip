@@ -7,12 +7,13 @@
 // vLLM-derived paged_attn.py page (_forward_prefix_pytorch: cached prefix unmasked, chunk causal).
 //
 // MI355X design (a dense contraction, so MFMA-bound):
-//   * work-group = 4 waves; tile = 128 query rows of one q head (32 rows per wave);
+//   * head_dim <= 128: work-group = 4 waves; tile = 128 query rows of one q head (32 rows per
+//     wave); head_dim 256: 12 waves x 16 rows, a 192-row tile;
 //   * head_dim <= 128: K and V tiles of BN keys go straight from HBM into LDS with direct-to-LDS
 //     loads (global_load_lds_dwordx4), K two tiles ahead and V one tile ahead in rings of 3 and
 //     2 tiles, their 16-byte units permuted within each row so that the MFMA operand reads are
 //     free of bank conflicts; one explicit wait and barrier per tile;
-//   * head_dim 256 (16-row form below): tiles are loaded into registers two tiles ahead and
+//   * head_dim 256 (16-row form below, 12 waves): tiles are loaded into registers a tile ahead and
 //     staged into padded LDS rows (direct-to-LDS loads measured slower there);
 //   * the QK^T MFMAs are scheduled with four LDS reads of K in flight;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the wave's Q rows held in
@@ -23,7 +24,8 @@
 //     cross the diagonal or the ragged end are masked;
 //   * work-groups are mapped to XCDs so that all q heads sharing one kv head run on one XCD
 //     (its L2 then serves the K/V re-reads of every head of the group);
-//   * q tiles are issued last-first (the longest causal rows start first).
+//   * (request, q tile) work items run longest-first (most visible keys first), from a schedule
+//     built on the host (passed with the launch) or, for long schedules, on the device.
 #include <math.h>
 
 #include <algorithm>
@@ -444,20 +446,24 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 // ------------------------------------------------------------------------------------------------
-// Variant with 16 query rows per wave on v_mfma_f32_16x16x32_bf16: 8 waves x 16 rows = the same
-// 128-row q tile, but each wave holds half the output accumulator and half the q rows, so two
-// waves fit on a SIMD at head_dim 256 (one wave's LDS and load latency is hidden by the other's
-// MFMA work). Each wave still reads the whole K / V tile from LDS, so LDS traffic per FLOP is
-// twice the 32-row form's.
+// Variant with 16 query rows per wave on v_mfma_f32_16x16x32_bf16, for head_dim 256: a wave holds
+// half the output accumulator and half the q rows of the 32-row form, so with one K / V tile of
+// register prefetch it fits 168 VGPRs and three waves share a SIMD. The kernel is bound by
+// latency (LDS reads feeding each MFMA, the per-tile barrier), not by a unit's throughput, so the
+// third wave per SIMD is what hides it: 12 waves x 16 rows measured 10 % faster than 8 waves with
+// two tiles of prefetch. Each wave still reads the whole K / V tile from LDS, so LDS traffic per
+// FLOP is twice the 32-row form's.
 //   S^T = K Q^T per 16-key tile: A = 16 K rows x 32 d (LDS), B = the wave's Q rows (registers);
 //     lane l holds keys 16*kt + 4*(l/16) + r of query l%16.
 //   O^T += V^T P^T per 32-key step: the lane's 8 probabilities (keys 4*(l/16) + j and
 //     16 + 4*(l/16) + j of the step) are its B operand as they stand; the A operand takes V^T
 //     with the same key order from two LDS transpose reads.
-constexpr int kP16Waves = 8;
+// 12 waves x 16 rows = a 192-row q tile; the first 8 waves load and stage the K / V tiles (a
+// 32-key tile is 1024 16-byte units: two per loading thread).
+constexpr int kP16Waves = 12;
 constexpr int kP16Threads = kP16Waves * kWave;
+constexpr int kP16LoadThreads = 8 * kWave;  // threads that load and stage K / V tiles
 constexpr int kP16BM = 16 * kP16Waves;  // query rows per work-group
-static_assert(kP16BM == kBM, "both prefill forms use the same q tile");
 
 template <int D>
 struct P16Cfg {
@@ -475,15 +481,15 @@ struct P16Cfg {
   static constexpr int BUF = BN * (RSE + RSV);     // one K+V tile buffer
   static constexpr int UPR = D / 8;                // 16-byte units per row
   static constexpr int UNITS = BN * UPR;           // units per tile (K or V)
-  static constexpr int UPT = UNITS / kP16Threads;  // units per thread
-  static constexpr int PF = (D >= 256) ? 2 : 1;    // kv tiles in flight in registers
+  static constexpr int UPT = UNITS / kP16LoadThreads;  // units per loading thread
+  static constexpr int PF = 1;                     // kv tiles in flight in registers
   static constexpr int LDS_ELEMS = (2 * BUF > kP16BM * RSE) ? 2 * BUF : kP16BM * RSE;
-  static_assert(UNITS % kP16Threads == 0, "tile units must divide evenly");
+  static_assert(UNITS % kP16LoadThreads == 0, "tile units must divide evenly");
   static_assert(kWave / UPR <= 16, "a wave's load rows must stay inside one block");
 };
 
 template <int D, bool PAGED>
-__global__ void __launch_bounds__(kP16Threads, 2)
+__global__ void __launch_bounds__(kP16Threads, kP16Waves / 4)
 prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
                  const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
@@ -519,7 +525,7 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qcol = lane & 15;  // query of this lane within the wave
   const int grp = lane >> 4;   // 0..3
   const int row = m0 + w * 16 + qcol;
@@ -555,13 +561,15 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // probabilities are exactly 0). Every call issues the same loads in the same order, whatever
   // n0 is, so the wait before each stage counts exactly the loads still needed.
   const int last_n0 = (n_kt - 1) * C::BN;  // first row of the last tile
+  const bool loader = w < kP16LoadThreads / kWave;  // wave-uniform
   auto fetch = [&](int n0, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
+    if (!loader) return;
     n0 = __builtin_amdgcn_readfirstlane(min(n0, last_n0));  // past the last tile: repeat it
     const int last_r = kv - 1 - n0;  // >= 0: the tile's last row inside the request
 #pragma unroll
     for (int i = 0; i < C::UPT; ++i) {
-      const int u = i * kP16Threads + tid;
+      const int u = i * kP16LoadThreads + tid;
       const int rr = u / C::UPR;
       const int cu = u - rr * C::UPR;
       const int r = min(rr, last_r);
@@ -569,7 +577,7 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       int off;      // per-lane byte offset
       if constexpr (PAGED) {
         // the instruction's first row: wave-uniform, in the same block as every row it loads
-        const int nb = min(n0 + (i * kP16Threads + w_u0) / C::UPR, kv - 1);
+        const int nb = min(n0 + (i * kP16LoadThreads + w_u0) / C::UPR, kv - 1);
         base = pl.block_offset(nb);
         off = (__umul24((n0 + r) & (BS - 1), D) + cu * 8) * 2;  // 24-bit products (host-checked)
       } else {
@@ -583,11 +591,12 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   };
   auto stash = [&](int buf, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
+    if (!loader) return;
     uint16_t* const k_lds = smem + buf * C::BUF;
     uint16_t* const v_lds = k_lds + C::BN * C::RSE;
 #pragma unroll
     for (int i = 0; i < C::UPT; ++i) {
-      const int u = i * kP16Threads + tid;
+      const int u = i * kP16LoadThreads + tid;
       const int rr = u / C::UPR;
       const int cu = u - rr * C::UPR;
       *reinterpret_cast<u32x4*>(k_lds + rr * C::RSE + cu * 8) = kpre[sl][i];
@@ -735,15 +744,17 @@ constexpr bool use_p16() {
 }
 
 // Keys a (request, q tile)'s rows can see: the work the longest-first schedule sorts by.
-static int64_t tile_work(int qo, int64_t kv, int qt, int causal) {
+static int64_t tile_work(int qo, int64_t kv, int qt, int causal, int bm) {
   int64_t vis = kv;
-  if (causal) vis = std::min<int64_t>(kv, (int64_t)(qt + 1) * kBM + kv - qo);
+  if (causal) vis = std::min<int64_t>(kv, (int64_t)(qt + 1) * bm + kv - qo);
   return std::max<int64_t>(vis, 0);
 }
 
-int64_t prefill_tile_count(int batch, const int32_t* qo_indptr_h) {
+int prefill_tile_rows(int head_dim) { return head_dim >= 256 ? kP16BM : kBM; }
+
+int64_t prefill_tile_count(int batch, const int32_t* qo_indptr_h, int bm) {
   int64_t n = 0;
-  for (int b = 0; b < batch; ++b) n += (qo_indptr_h[b + 1] - qo_indptr_h[b] + kBM - 1) / kBM;
+  for (int b = 0; b < batch; ++b) n += (qo_indptr_h[b + 1] - qo_indptr_h[b] + bm - 1) / bm;
   return n;
 }
 
@@ -766,9 +777,9 @@ static void build_order(const PrefillArgs& a, TileOrder& ord) {
     const int64_t kv = a.kv_indptr_h ? (int64_t)a.kv_indptr_h[b + 1] - a.kv_indptr_h[b]
                                      : std::min<int64_t>(std::max(a.kv_lens_h[b], 0),
                                                          (int64_t)a.max_blocks_per_seq * a.block_size);
-    const int n_qt = (qo + kBM - 1) / kBM;
+    const int n_qt = (qo + a.tile_rows - 1) / a.tile_rows;
     for (int qt = 0; qt < n_qt; ++qt)
-      items.push_back({tile_work(qo, kv, qt, a.causal), ((uint32_t)b << 16) | (uint32_t)qt});
+      items.push_back({tile_work(qo, kv, qt, a.causal, a.tile_rows), ((uint32_t)b << 16) | (uint32_t)qt});
   }
   std::stable_sort(items.begin(), items.end(),
                    [](const Item& x, const Item& y) { return x.work > y.work; });
@@ -789,7 +800,7 @@ constexpr int kPlanPerThread = kPlanBuckets / kPlanThreads;
 __global__ void __launch_bounds__(kPlanThreads)
 prefill_plan_kernel(const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
                     const int32_t* __restrict__ kv_lens, int batch, int causal, int total_q,
-                    int total_kv, int kv_cap, uint32_t* __restrict__ order, int capacity) {
+                    int total_kv, int kv_cap, int bm, uint32_t* __restrict__ order, int capacity) {
   __shared__ int hist[kPlanBuckets];
   __shared__ int wave_sum[kPlanThreads / kWave];
   const int tid = threadIdx.x;
@@ -807,13 +818,13 @@ prefill_plan_kernel(const int32_t* __restrict__ qo_indptr, const int32_t* __rest
   };
   auto bucket = [&](int qo, int kv, int qt) {
     int vis = kv;
-    if (causal) vis = (int)clampi<int64_t>((int64_t)(qt + 1) * kBM + kv - qo, 0, kv);
+    if (causal) vis = (int)clampi<int64_t>((int64_t)(qt + 1) * bm + kv - qo, 0, kv);
     return kPlanBuckets - 1 - min((vis + 31) >> 5, kPlanBuckets - 1);
   };
   for (int b = tid; b < batch; b += kPlanThreads) {
     int qo, kv;
     extents(b, qo, kv);
-    const int n_qt = min((qo + kBM - 1) / kBM, 0xffff);
+    const int n_qt = min((qo + bm - 1) / bm, 0xffff);
     for (int qt = 0; qt < n_qt; ++qt) atomicAdd(&hist[bucket(qo, kv, qt)], 1);
   }
   __syncthreads();
@@ -846,7 +857,7 @@ prefill_plan_kernel(const int32_t* __restrict__ qo_indptr, const int32_t* __rest
   for (int b = tid; b < batch; b += kPlanThreads) {
     int qo, kv;
     extents(b, qo, kv);
-    const int n_qt = min((qo + kBM - 1) / kBM, 0xffff);
+    const int n_qt = min((qo + bm - 1) / bm, 0xffff);
     for (int qt = 0; qt < n_qt; ++qt) {
       const int pos = atomicAdd(&hist[bucket(qo, kv, qt)], 1);
       if (pos < capacity) order[pos] = ((uint32_t)b << 16) | (uint32_t)qt;
@@ -867,7 +878,7 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
   } else {
     hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.qo_indptr,
                        a.kv_indptr, a.kv_lens, a.batch, a.causal, a.total_q, (int)a.total_kv, kv_cap,
-                       (uint32_t*)a.workspace, (int)a.tiles);
+                       a.tile_rows, (uint32_t*)a.workspace, (int)a.tiles);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     order_dev = (const uint32_t*)a.workspace;
