@@ -138,7 +138,7 @@ class Case:
         return self.work / (ms * 1e-3) / (1e12 if self.kind == "mfma" else 1e9)
 
 
-def build_cases(dev):
+def build_cases(dev, tune=True):
     cases = {}
     # workload 5: scatter + paged prefill
     ci = make_config(5)
@@ -202,9 +202,15 @@ def build_cases(dev):
         dtok = {"seqs_per_s": B, "kv_tokens_per_s": sum(lens)}
         cases[key] = Case(f"paged_attn_decode ({CONFIGS[cid]['name']}, B={B}, {Hq}/{Hkv} heads, hd {D})",
                           mk(), "hbm", work, "GB/s", dtok)
-        # the measured plan for this shape (pkv_decode_tune, once at set-up)
-        plan = pkv.decode_tune(c["q"], c["kc"], c["vc"], c["bt"], c["sl"], c["scale"], max_seq_len=c["msl"],
-                               repeats=5, out=c["out"])
+        # the measured plan for this shape (pkv_decode_tune, once at set-up); without tuning, the
+        # library's default choice as a plan
+        if tune:
+            plan = pkv.decode_tune(c["q"], c["kc"], c["vc"], c["bt"], c["sl"], c["scale"], max_seq_len=c["msl"],
+                                   repeats=5, out=c["out"])
+        else:
+            _, dpt, dws = pkv.decode_plan(lens, Hq, Hkv, D, pt)
+            plan = pkv.DecodePlan(partition_tokens=dpt, partitions_per_wave=0, max_seq_len=di.max_seq_len,
+                                  workspace_bytes=dws)
         c["plan"] = plan
         c["ws_plan"] = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
 
@@ -462,6 +468,12 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="skip the decode tuning sweep at set-up (for profiler runs; the *_tuned lines then "
+                         "run the default plan)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated calls to time (default: all); a profiler run of one call then sees "
+                         "only that call's kernels in the timed region")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library's hot path runs on a single MI355X and no "
@@ -477,8 +489,19 @@ def main():
         calibrate_copy(dev)
         return
     print(f"# device: {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
-    cases, meta = build_cases(dev)
+    cases, meta = build_cases(dev, tune=not args.no_tune)
     print("# inputs resident; timing", file=sys.stderr, flush=True)
+    if args.only:
+        only = [k for k in args.only.split(",") if k]
+        unknown = [k for k in only if k not in cases]
+        if unknown:
+            sys.exit(f"unknown calls {unknown}; known: {sorted(cases)}")
+        for k in only:
+            time_alone(cases[k], reps=args.steps, warmup=args.warmup)
+            c = cases[k]
+            print(json.dumps({"call": k, "name": c.name, "avg_ms": round(statistics.fmean(c.ms), 5),
+                              "rate": round(c.rate(statistics.fmean(c.ms)), 2), "unit": c.unit}), flush=True)
+        return
     ms_step, wall = time_step(cases, args.steps, args.warmup)
     for k in EXTRA:
         time_alone(cases[k])

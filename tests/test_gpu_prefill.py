@@ -43,6 +43,8 @@ RAGGED_EDGE = [
     ([129, 5, 300], None, 8, 1, 128, True),         # group of 8 rows, 6 rows used
     ([129, 40, 1], [129, 90, 1], 16, 4, 256, True), # group of 2 rows, 4 rows, head_dim 256
     ([1] * 801, [37] * 801, 8, 2, 128, True),       # device-built schedule, groups of 4 rows
+    ([1] * 790, [50] * 790, 4, 2, 256, True),       # device-built schedule of 192-row q tiles
+    ([400, 193, 192, 1], [600, 193, 300, 9], 8, 2, 256, True),  # 192-row q tiles and their edges
 ]
 
 
