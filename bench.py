@@ -58,16 +58,16 @@ METRIC = "decode KV GB/s (% HBM peak); ragged-prefill bf16 TFLOP/s (% MFMA peak)
 # mismatch reports traffic as null.
 CSRC = os.path.join(ROOT, "paged_kv_cache_232_amd", "csrc")
 TRAFFIC = {
-    "scatter5": (("cache.hip",), "ca92b19357222b29", 71237760),
-    "paged5": (("prefill.hip", "common.h"), "d01ca26c8a88fa21", 547159808),
-    "ragged2": (("prefill.hip", "common.h"), "d01ca26c8a88fa21", 194950400),
-    "decode3": (("decode.hip", "common.h"), "129d7b34160e5974", 1019179690),
-    "decode3_direct": (("decode.hip", "common.h"), "129d7b34160e5974", 1019121664),
-    "decode3_split": (("decode.hip", "common.h"), "129d7b34160e5974", 1039546766),
-    "decode4": (("decode.hip", "common.h"), "129d7b34160e5974", 2220511018),
-    "decode3_fp8": (("decode.hip", "common.h"), "129d7b34160e5974", 510820060),
-    "decode4_fp8": (("decode.hip", "common.h"), "129d7b34160e5974", 1146875398),
-    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073888389),
+    "scatter5": (("cache.hip",), "ca92b19357222b29", 71236009),
+    "paged5": (("prefill.hip", "common.h"), "97a8c059352b6c06", 513111299),
+    "ragged2": (("prefill.hip", "common.h"), "97a8c059352b6c06", 195426223),
+    "decode3": (("decode.hip", "common.h"), "087d5755d82003db", 1019061981),
+    "decode3_direct": (("decode.hip", "common.h"), "087d5755d82003db", 1019061981),
+    "decode3_split": (("decode.hip", "common.h"), "087d5755d82003db", 1039480541),
+    "decode4": (("decode.hip", "common.h"), "087d5755d82003db", 2220423475),
+    "decode3_fp8": (("decode.hip", "common.h"), "087d5755d82003db", 510457540),
+    "decode4_fp8": (("decode.hip", "common.h"), "087d5755d82003db", 1146829052),
+    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073876141),
 }
 
 
