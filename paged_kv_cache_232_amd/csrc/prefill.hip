@@ -142,8 +142,16 @@ __device__ __forceinline__ bool resolve_tile(int y, const TileOrder& order,
                                              int total_q, int total_kv, int kv_cap, TileWork& t) {
   // made explicitly wave-uniform: the request's extents then stay scalar, and so do the block-table
   // reads the tile loads address from (a vector table read would wait for every load in flight)
-  const uint32_t sched = (uint32_t)__builtin_amdgcn_readfirstlane(
-      (int)(order_dev != nullptr ? order_dev[y] : order.e[min(y, kMaxOrder - 1)]));
+  // two separate reads (a select of the two pointers would make one flat load of a generic
+  // address, a vector load waited on in full, in place of a scalar load)
+  uint32_t sched;
+  if (order_dev != nullptr) {
+    sched = order_dev[y];
+  } else {
+    sched = order.e[min(y, kMaxOrder - 1)];
+    __asm__ volatile("" : "+s"(sched));  // keeps the two reads apart
+  }
+  sched = (uint32_t)__builtin_amdgcn_readfirstlane((int)sched);
   if (sched == kNoTile) return false;
   t.b = (int)(sched >> 16);
   t.qt = (int)(sched & 0xffffu);
@@ -232,19 +240,8 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int row = m0 + w * 32 + qcol;     // query row within the request
   const bool row_ok = row < qo;
 
-  // Q^T operand: lane holds Q[row][ks*16 + 8*half .. +8]
+  // Q^T operand: lane holds Q[row][ks*16 + 8*half .. +8] (loaded after the first tiles, below)
   bf16x8 qreg[C::KS];
-  {
-    const int r = row_ok ? row : (qo - 1);
-    const uint16_t* qp = q + ((size_t)(q0 + r) * Hq + h) * D + 8 * half;
-    const uint32_t flip = negate_q ? 0x80008000u : 0u;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 x = load16(qp + ks * 16);
-      x ^= u32x4{flip, flip, flip, flip};
-      qreg[ks] = as_bf16x8(x);
-    }
-  }
 
   f32x16 o[C::DT];
 #pragma unroll
@@ -332,6 +329,19 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     load_tile(k, 0, k_lds_of(0));
     load_tile(v, 0, v_lds_of(0));
     if (n_kt > 1) load_tile(k, 1, k_lds_of(1));
+  }
+  // q rows are loaded after the first tiles' loads are issued, so those queue first (2-3 % faster
+  // on the ragged prefill than the other order)
+  {
+    const int r = row_ok ? row : (qo - 1);
+    const uint16_t* qp = q + ((size_t)(q0 + r) * Hq + h) * D + 8 * half;
+    const uint32_t flip = negate_q ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 x = load16(qp + ks * 16);
+      x ^= u32x4{flip, flip, flip, flip};
+      qreg[ks] = as_bf16x8(x);
+    }
   }
   // last key any row of this wave can see (causal): tiles past it are skipped by the wave; a wave
   // whose rows all lie past the request's end (the q tile's padding) skips every tile
@@ -562,6 +572,18 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // n0 is, so the wait before each stage counts exactly the loads still needed.
   const int last_n0 = (n_kt - 1) * C::BN;  // first row of the last tile
   const bool loader = w < kP16LoadThreads / kWave;  // wave-uniform
+  // Paged: the physical blocks a fetch reads are looked up one fetch ahead, so the block-table
+  // reads (scalar loads) complete under the wait that precedes the next barrier instead of
+  // stalling the fetch that needs them.
+  int blk_next[C::UPT];
+  auto lookup = [&](int n0) {
+    if constexpr (PAGED) {
+      n0 = __builtin_amdgcn_readfirstlane(min(n0, last_n0));
+#pragma unroll
+      for (int i = 0; i < C::UPT; ++i)  // raw entries: clamped where they are used
+        blk_next[i] = pl.row[(min(n0 + (i * kP16LoadThreads + w_u0) / C::UPR, kv - 1)) >> bs_shift];
+    }
+  };
   auto fetch = [&](int n0, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
     if (!loader) return;
@@ -576,9 +598,9 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       size_t base;  // wave-uniform element offset
       int off;      // per-lane byte offset
       if constexpr (PAGED) {
-        // the instruction's first row: wave-uniform, in the same block as every row it loads
-        const int nb = min(n0 + (i * kP16LoadThreads + w_u0) / C::UPR, kv - 1);
-        base = pl.block_offset(nb);
+        // the instruction's first row is wave-uniform and in the same block as every row it
+        // loads; its block was looked up by the previous fetch
+        base = ((size_t)clampi(blk_next[i], 0, NB - 1) * Hkv + kh) * BS * D;
         off = (__umul24((n0 + r) & (BS - 1), D) + cu * 8) * 2;  // 24-bit products (host-checked)
       } else {
         base = rl.row_offset(n0);
@@ -588,6 +610,7 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       vpre[sl][i] = buffer_load16(buffer_at(v + base), off);
       memory_order_point();
     }
+    lookup(n0 + C::BN);
   };
   auto stash = [&](int buf, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
@@ -611,6 +634,7 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, (C::PF > 1) ? 1 : 0>;
   if (n_kt > 0) {
+    if (loader) lookup(0);
     fetch(0, S0{});
     stash(0, S0{});
     fetch(C::BN, S1{});
