@@ -66,7 +66,6 @@ TRAFFIC = {
     "decode3_split": (("decode.hip", "common.h"), "087d5755d82003db", 1039480541),
     "decode4": (("decode.hip", "common.h"), "087d5755d82003db", 2220423475),
     "decode3_fp8": (("decode.hip", "common.h"), "087d5755d82003db", 510457540),
-    "decode4_fp8": (("decode.hip", "common.h"), "087d5755d82003db", 1146829052),
     "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073876141),
 }
 
@@ -272,12 +271,18 @@ def build_cases(dev, tune=True):
         c["kc8"] = (c["kc"].float() / c["k_scale"]).to(torch.float8_e4m3fn).view(torch.uint8)
         c["vc8"] = (c["vc"].float() / c["v_scale"]).to(torch.float8_e4m3fn).view(torch.uint8)
 
-        def mk8(c=c, pt=pt):
+        # (the library's own path choice: direct for the batched workload, 4096-token partitions
+        # for the long contexts)
+        _, pt8, _ = pkv.decode_plan(lens, Hq, Hkv, D)
+
+        def mk8(c=c):
             return lambda: pkv.paged_attn_decode(c["q"], c["kc8"], c["vc8"], c["bt"], c["sl"], c["scale"],
-                                                 max_seq_len=c["msl"], partition_tokens=pt, out=c["out"],
+                                                 max_seq_len=c["msl"], partition_tokens=-1, out=c["out"],
                                                  workspace=c["ws"], k_scale=c["k_scale"], v_scale=c["v_scale"])
-        cases[key + "_fp8"] = Case(f"paged_attn_decode_fp8 ({CONFIGS[cid]['name']} over an e4m3 cache)", mk8(),
-                                   "hbm", decode_bytes_fp8(lens, Hq, Hkv, D, di.block_size), "GB/s", dtok)
+        path8 = "direct" if pt8 == 0 else f"split {pt8}"
+        cases[key + "_fp8"] = Case(f"paged_attn_decode_fp8 ({CONFIGS[cid]['name']} over an e4m3 cache, library's "
+                                   f"choice: {path8})", mk8(), "hbm",
+                                   decode_bytes_fp8(lens, Hq, Hkv, D, di.block_size), "GB/s", dtok)
         meta[f"lens{cid}_sum"] = sum(lens)
         meta[f"flops{cid}"] = decode_flops(lens, Hq, D)
         del di

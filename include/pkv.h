@@ -104,7 +104,10 @@ int pkv_decode_plan(const int32_t* seq_lens_h, int32_t batch, int32_t num_q_head
  *   block_tables [batch, max_blocks_per_seq] int32; seq_lens [batch] int32.
  *   max_seq_len  host hint: must be >= every seq_lens[b]; sizes the split grid. Lengths are also
  *                clamped to max_blocks_per_seq * block_size.
- *   partition_tokens  0 = direct; > 0 = split (a multiple of 32); -1 = library choice.
+ *   partition_tokens  0 = direct; > 0 = split (a multiple of 32); -1 = library choice: direct
+ *                when batch * num_kv_heads * ceil(group / 16) >= 512 or max_seq_len <= 512, else
+ *                split with the longest power-of-two partition from 512 to 8192 tokens that still
+ *                gives 1024 partitions of (sequence, kv head, 16-head group) at max_seq_len.
  *   workspace    device scratch of at least pkv_decode_workspace_bytes(...) bytes (may be NULL
  *                when that is 0). Its contents need no initialisation.
  */
@@ -120,7 +123,7 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
  * PagedAttentionBf16::new plans direct vs split decode and keeps the profiling state
  * (profile_allowed, tuning_complete) of a CUDA autotuner so the choice is timed on the device.
  * pkv_decode_tune times, on the caller's own buffers and stream, the library's default choice,
- * the direct path, and split-KV with partitions of 256 / 512 / 1024 / 2048 tokens streamed 1, 2,
+ * the direct path, and split-KV with partitions of 256 to 8192 tokens (powers of two) streamed 1, 2,
  * 4, 8 or 16 to a wave (those whose partials fit the LDS budget and the given workspace), each
  * the median of `repeats` launches after one untimed launch, and writes the fastest into *plan.
  * The default choice is a candidate, so the plan is never slower than it on that measurement.

@@ -144,9 +144,11 @@ def test_workspace_bytes():
     want = al(B * Hq * P * D * 4) + 2 * al(B * Hq * P * 4)
     assert lib.pkv_decode_workspace_bytes(B, Hq, 8, D, L, 512) == want
     # library choice: direct from two (sequence, kv head) work-groups per CU (512) upwards, else
-    # split 512 when the context is longer than one partition
+    # split when the context is longer than one partition; 256 groups x 8192 tokens give 1024
+    # partitions of 2048 tokens
     assert lib.pkv_decode_workspace_bytes(B, Hq, 8, D, L, -1) == 0
-    want_half = al(B // 2 * Hq * P * D * 4) + 2 * al(B // 2 * Hq * P * 4)
+    P2 = L // 2048
+    want_half = al(B // 2 * Hq * P2 * D * 4) + 2 * al(B // 2 * Hq * P2 * 4)
     assert lib.pkv_decode_workspace_bytes(B // 2, Hq, 8, D, L, -1) == want_half
     assert lib.pkv_decode_workspace_bytes(B // 2, Hq, 8, D, 512, -1) == 0
 
@@ -181,6 +183,12 @@ def test_decode_plan_uses_the_real_maximum():
     assert pkv.decode_plan([4096] * 64, 32, 8, 128)[1] == 0
     # short sequences stay direct whatever the batch
     assert pkv.decode_plan([300, 512], 32, 8, 128)[1] == 0
+    # long contexts: the partition doubles from 512 while the longest sequence still gives 1024
+    # (sequence, kv head, head group) partitions, up to 8192 tokens
+    assert pkv.decode_plan([131072] * 4, 64, 8, 128)[1] == 4096   # 32 groups x 32 partitions
+    assert pkv.decode_plan([131072], 32, 8, 128)[1] == 1024       # 8 groups x 128 partitions
+    assert pkv.decode_plan([65536] * 16, 64, 8, 128)[1] == 8192   # capped
+    assert pkv.decode_plan([600], 8, 8, 64)[1] == 512             # too short to fill: the floor
     assert pkv.decode_plan([], 32, 8, 128) == (0, 0, 0)
     with pytest.raises(pkv.PkvError):
         pkv.decode_plan([5, -1], 32, 8, 128)
