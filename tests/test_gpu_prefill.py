@@ -58,6 +58,20 @@ def test_ragged_prefill_edge_shapes(case):
     assert_parity(out, ref, f"ragged edge {RAGGED_EDGE[case]}")
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(4, 2, 128), (8, 2, 64), (3, 3, 128), (16, 4, 256)])
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_ragged_prefill_negative_and_zero_scale(hq, hkv, d, scale):
+    """A negative scale (the kernels flip q's sign bits and keep a positive scale) and a zero one
+    (uniform weights), at head_dim 64, 128 (even and odd GQA groups) and 256."""
+    ri = ragged_prefill_inputs(2600 + hq + d, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, qo_lens=[150, 9, 300],
+                               kv_lens=[200, 9, 300], causal=True)
+    ref = oracle.ragged_prefill(ri.q, ri.k, ri.v, ri.qo_indptr, ri.kv_indptr, True, scale)
+    out = pkv.ragged_prefill(ri.q.to(DEV), ri.k.to(DEV), ri.v.to(DEV), ri.qo_indptr.to(DEV), ri.kv_indptr.to(DEV),
+                             True, scale, qo_indptr_h=ri.qo_indptr, kv_indptr_h=ri.kv_indptr)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu(), ref, f"ragged scale {scale} ({hq}/{hkv} heads, hd {d})")
+
+
 def test_ragged_prefill_config_full():
     ri = make_config(2)
     ref = oracle.ragged_prefill(ri.q, ri.k, ri.v, ri.qo_indptr, ri.kv_indptr, ri.causal, ri.scale)
