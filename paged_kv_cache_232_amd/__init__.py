@@ -487,12 +487,31 @@ def copy_blocks(k_caches, v_caches, block_mapping: torch.Tensor) -> None:
     _need(block_mapping, "block_mapping", torch.int64, 2, dev)
     if block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [n, 2]")
-    kp = torch.tensor([c.data_ptr() for c in k_caches], dtype=torch.int64).to(dev)
-    vp = torch.tensor([c.data_ptr() for c in v_caches], dtype=torch.int64).to(dev)
+    kp, vp = _layer_pointer_arrays(k_caches, v_caches, dev)
     _check(lib.pkv_copy_blocks(_ptr(kp), _ptr(vp), len(k_caches), _ptr(block_mapping), block_mapping.shape[0],
                                _block_bytes(ref), ref.shape[0], _stream(ref)), "copy_blocks")
-    # kp / vp may be freed on return: the caching allocator reuses their memory only for work
-    # ordered after this launch on the same stream
+
+
+# Device arrays of the layers' cache addresses, kept per (addresses, device): a serving loop calls
+# copy_blocks with the same caches every step, and uploading the arrays each time cost more than a
+# tenth of the call. The arrays hold addresses only, so they stay valid for any tensors that occupy
+# those addresses. A few recent sets are kept.
+_PTR_ARRAYS: "dict" = {}
+_PTR_ARRAYS_MAX = 8
+
+
+def _layer_pointer_arrays(k_caches, v_caches, dev):
+    key = (dev.index, tuple(c.data_ptr() for c in k_caches), tuple(c.data_ptr() for c in v_caches))
+    hit = _PTR_ARRAYS.get(key)
+    if hit is None:
+        if len(_PTR_ARRAYS) >= _PTR_ARRAYS_MAX:
+            torch.cuda.synchronize(dev)  # no launch on any stream still reads the oldest set
+            _PTR_ARRAYS.pop(next(iter(_PTR_ARRAYS)))
+        kp = torch.tensor(key[1], dtype=torch.int64).to(dev)
+        vp = torch.tensor(key[2], dtype=torch.int64).to(dev)
+        torch.cuda.current_stream(dev).synchronize()  # uploaded before any later stream may use them
+        hit = _PTR_ARRAYS[key] = (kp, vp)
+    return hit
 
 
 def swap_blocks(src: torch.Tensor, dst: torch.Tensor, block_mapping) -> None:

@@ -39,6 +39,32 @@ def test_copy_blocks_bit_exact(layers, nb, hkv, bs, d, npairs):
         assert np.array_equal(vd[l].cpu().view(torch.int16).numpy(), ev[l]), f"V layer {l}"
 
 
+def test_copy_blocks_repeated_calls_over_changing_cache_sets():
+    """A serving loop's pattern: the same layers called again with new mappings, interleaved with
+    other cache sets, more sets than the binding keeps address arrays for, and a set whose tensors
+    are freed and reallocated. Every call is checked bit-exact against the oracle."""
+    g = torch.Generator().manual_seed(77)
+    nb, shape = 24, (24, 2, 16, 64)
+    sets = []
+    for i in range(11):
+        layers = 1 + i % 3
+        sets.append(([_random_cache(g, shape).to(DEV) for _ in range(layers)],
+                     [_random_cache(g, shape).to(DEV) for _ in range(layers)]))
+    for step in range(30):
+        i = (step * 7) % len(sets) if step % 3 else 0  # set 0 recurs; the others cycle past the limit
+        kd, vd = sets[i]
+        m = _mapping(g, nb, 5)
+        ek, ev = oracle.copy_blocks([c.cpu() for c in kd], [c.cpu() for c in vd], m)
+        pkv.copy_blocks(kd, vd, m.to(DEV))
+        torch.cuda.synchronize()
+        for l in range(len(kd)):
+            assert np.array_equal(kd[l].cpu().view(torch.int16).numpy(), ek[l]), f"step {step} K layer {l}"
+            assert np.array_equal(vd[l].cpu().view(torch.int16).numpy(), ev[l]), f"step {step} V layer {l}"
+        if step == 10:
+            # free set 1 and allocate new caches (possibly at the same addresses)
+            sets[1] = ([_random_cache(g, shape).to(DEV)], [_random_cache(g, shape).to(DEV)])
+
+
 def test_copy_blocks_empty_mapping_is_noop():
     g = torch.Generator().manual_seed(5)
     kc = _random_cache(g, (8, 2, 16, 64)).to(DEV)
