@@ -260,12 +260,23 @@ int pkv_validate_block_tables_h(const int32_t* block_tables_h, const int32_t* se
                                 int32_t num_blocks);
 
 /*
- * paged_attn_decode with a sliding window: as pkv_paged_attn_decode (same arguments, paths and
- * workspace), with sequence b attending only to its keys [max(0, seq_lens[b] - window), seq_lens[b]).
- * window == 0 means no window; window < 0 is PKV_E_INVALID_ARGUMENT. The vLLM-derived paged_attn.py
- * page's forward_decode takes a sliding_window, and the libmir-cuda page sizes its split partitions
- * by (token_count, window) (captured_configs).
+ * paged_attn_decode with a sliding window: as pkv_paged_attn_decode (same arguments and output),
+ * with sequence b attending only to its keys [max(0, seq_lens[b] - window), seq_lens[b]).
+ * window == 0 means no window (then exactly pkv_paged_attn_decode); window < 0 is
+ * PKV_E_INVALID_ARGUMENT. The vLLM-derived paged_attn.py page's forward_decode takes a
+ * sliding_window, and the libmir-cuda page sizes its split partitions by (token_count, window)
+ * (captured_configs). Likewise here, with window > 0:
+ *   partition_tokens -1 plans on min(max_seq_len, window) keys (the rule of pkv_paged_attn_decode);
+ *   a split call's partials cover only the partitions a window can touch, so its workspace is
+ *   pkv_decode_window_workspace_bytes(...), at most what pkv_decode_workspace_bytes gives for the
+ *   same partition size.
  */
+/* Workspace bytes pkv_paged_attn_decode_window needs (0 on its direct path); window == 0 gives
+ * pkv_decode_workspace_bytes. Arguments as for pkv_paged_attn_decode_window. */
+size_t pkv_decode_window_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_seq_len, int32_t window,
+                                         int32_t partition_tokens);
+
 int pkv_paged_attn_decode_window(const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* block_tables, const int32_t* seq_lens, void* out,
                                  float* lse, int32_t batch, int32_t num_q_heads,

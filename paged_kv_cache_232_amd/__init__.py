@@ -48,6 +48,7 @@ _SIGNATURES = {
     "pkv_reshape_and_cache": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32,
                                              _c_i32, _c_i32, _c_i32, _c_ptr]),
     "pkv_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_decode_window_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pkv_paged_attn_decode": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                              _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                              _c_i32, _c_f32, _c_i32, _c_ptr, _c_size, _c_ptr]),
@@ -196,6 +197,13 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head
                                                           max_seq_len, partition_tokens))
 
 
+def decode_window_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                  max_seq_len: int, window: int, partition_tokens: int = -1) -> int:
+    """Workspace bytes of a sliding-window decode (pkv_decode_window_workspace_bytes)."""
+    return int(load_library().pkv_decode_window_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                                 max_seq_len, window, partition_tokens))
+
+
 def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, *,
                       max_seq_len: Optional[int] = None, partition_tokens: int = -1,
@@ -235,7 +243,12 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         if fp8 or window:
             raise ValueError("a tuned plan runs bf16 caches without a window")
         partition_tokens = plan.partition_tokens
-    need = decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len, partition_tokens) if B else 0
+    if not B:
+        need = 0
+    elif window and plan is None:
+        need = decode_window_workspace_bytes(B, Hq, Hkv, D, max_seq_len, int(window), partition_tokens)
+    else:
+        need = decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len, partition_tokens)
     workspace = _need_workspace(workspace, need, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if plan is not None:

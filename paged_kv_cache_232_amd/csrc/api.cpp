@@ -111,6 +111,23 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
   return pkv::decode_workspace_layout(batch, num_q_heads, head_dim, max_seq_len, pt).total;
 }
 
+size_t pkv_decode_window_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_seq_len, int32_t window,
+                                         int32_t partition_tokens) {
+  if (window <= 0)
+    return pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                      partition_tokens);
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0)
+    return 0;
+  if (num_q_heads % num_kv_heads != 0) return 0;
+  const int pt = resolve_partition(batch, num_q_heads, num_kv_heads,
+                                   std::min(max_seq_len, window), partition_tokens);
+  if (pt <= 0) return 0;
+  return pkv::decode_workspace_layout_p(batch, num_q_heads, head_dim,
+                                        pkv::decode_window_partitions(max_seq_len, window, pt))
+      .total;
+}
+
 }  // extern "C"
 
 int pkv::decode_checked(const void* q, const void* k_cache, const void* v_cache,
@@ -157,11 +174,17 @@ int pkv::decode_checked(const void* q, const void* k_cache, const void* v_cache,
   a.v_scale = v_scale;
   a.window = window;
   a.ppw_override = ppw_override;
-  a.partition_tokens =
-      resolve_partition(batch, num_q_heads, num_kv_heads, max_seq_len, partition_tokens);
+  // a windowed call is planned on the keys it can see, and its partials cover only the window
+  a.partition_tokens = resolve_partition(batch, num_q_heads, num_kv_heads,
+                                         window > 0 ? std::min(max_seq_len, window) : max_seq_len,
+                                         partition_tokens);
   if (a.partition_tokens > 0) {
-    const pkv::DecodeWorkspaceLayout wl = pkv::decode_workspace_layout(
-        batch, num_q_heads, head_dim, max_seq_len, a.partition_tokens);
+    const pkv::DecodeWorkspaceLayout wl =
+        window > 0 ? pkv::decode_workspace_layout_p(
+                         batch, num_q_heads, head_dim,
+                         pkv::decode_window_partitions(max_seq_len, window, a.partition_tokens))
+                   : pkv::decode_workspace_layout(batch, num_q_heads, head_dim, max_seq_len,
+                                                  a.partition_tokens);
     if (wl.max_partitions > 65535) return PKV_E_UNSUPPORTED;
     if (workspace == nullptr || workspace_bytes < wl.total) return PKV_E_WORKSPACE_TOO_SMALL;
     if (!aligned16(workspace)) return PKV_E_INVALID_ARGUMENT;

@@ -129,14 +129,17 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
   }
 
   int L = clampi(lens[b], 0, max_blocks * BS);
-  if constexpr (SPLIT) L = min(L, Pmax * PT);
+  if (SPLIT && window == 0) L = min(L, Pmax * PT);
   // sliding window: keys [t_lo, L); chunks stay 32-token aligned, keys before t_lo are masked
   const int t_lo = window > 0 ? max(0, L - window) : 0;
+  // windowed split: grid x and the partials count partitions from the one holding t_lo
+  const int p_base = (SPLIT && window > 0) ? t_lo / PT : 0;
   int t_begin = t_lo & ~31, t_end = L;
   if constexpr (SPLIT) {
-    // partitions p*ppw .. p*ppw + ppw - 1, streamed by one wave
-    t_begin = max(p * ppw * PT, t_begin);
-    t_end = min(L, (p * ppw + ppw) * PT);
+    // partitions p_base + p*ppw .. + ppw - 1, streamed by one wave
+    const int pa = p_base + p * ppw;
+    t_begin = max(pa * PT, t_begin);
+    t_end = min(L, (pa + ppw) * PT);
     if (t_begin >= t_end) return;  // uniform over the work-group (no partial is written)
   }
   const int p_first = SPLIT ? t_begin / PT : 0;  // partition of the first chunk
@@ -387,7 +390,7 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
     const float inv = l_run > 0.f ? v_scale / l_run : 0.f;
     if constexpr (SPLIT) {
       const int p_last = (t_end - 1) / PT;
-      const size_t pi = ((size_t)b * Pmax + p_last) * Hq + hout;
+      const size_t pi = ((size_t)b * Pmax + (p_last - p_base)) * Hq + hout;
       float* op = o_part + pi * D + 4 * qg;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) *reinterpret_cast<f32x4*>(op + mt * 16) = o[mt] * inv;
@@ -398,7 +401,7 @@ decode_kernel(const uint16_t* __restrict__ q, const std::conditional_t<FP8, uint
       // the parked partitions p_first .. p_last - 1
       for (int pp = p_first; pp < p_last; ++pp) {
         const float* sl = stage + (pp - p_first) * slot_floats;
-        const size_t pj = ((size_t)b * Pmax + pp) * Hq + hout;
+        const size_t pj = ((size_t)b * Pmax + (pp - p_base)) * Hq + hout;
         float* fp = o_part + pj * D + 4 * qg;
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt)
@@ -544,11 +547,11 @@ decode_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ 
   const int b = blockIdx.y;
   const int t = threadIdx.x;
   int L = clampi(lens[b], 0, max_blocks * BS);
-  L = min(L, Pmax * PT);
-  const int P = (L + PT - 1) / PT;  // partitions holding tokens (each has a finite max)
-  // a sliding window leaves the partitions before its first key unwritten
+  if (window == 0) L = min(L, Pmax * PT);
+  // a sliding window's partials start at the partition holding its first key
   const int p_lo = window > 0 ? max(0, L - window) / PT : 0;
-  // partial p of (b, h) is row (b * Pmax + p) * Hq + h
+  const int P = min((L + PT - 1) / PT, p_lo + Pmax);  // partitions holding tokens (finite max each)
+  // partial p of (b, h) is row (b * Pmax + p - p_lo) * Hq + h
   const size_t pi0 = (size_t)b * Pmax * Hq + h;
   const int u = t % U;
   const int g = t / U;
@@ -566,7 +569,7 @@ decode_merge_kernel(const float* __restrict__ o_part, const float* __restrict__ 
       mp[j] = -INFINITY;
       lp[j] = 0.f;
       if (p < P) {
-        const size_t pi = pi0 + (size_t)p * Hq;
+        const size_t pi = pi0 + (size_t)(p - p_lo) * Hq;
         x[j] = reinterpret_cast<const f32x4*>(o_part + pi * D)[u];
         mp[j] = m_part[pi];
         lp[j] = l_part[pi];
@@ -622,9 +625,20 @@ int decode_max_ppw(int num_q_heads, int num_kv_heads, int head_dim) {
 
 DecodeWorkspaceLayout decode_workspace_layout(int batch, int num_q_heads, int head_dim,
                                               int max_seq_len, int partition_tokens) {
-  DecodeWorkspaceLayout w{0, 0, 0, 0, 0};
-  if (partition_tokens <= 0) return w;
+  if (partition_tokens <= 0) return DecodeWorkspaceLayout{0, 0, 0, 0, 0};
   const int P = max_seq_len > 0 ? (max_seq_len + partition_tokens - 1) / partition_tokens : 1;
+  return decode_workspace_layout_p(batch, num_q_heads, head_dim, P);
+}
+
+int decode_window_partitions(int max_seq_len, int window, int partition_tokens) {
+  const int all = max_seq_len > 0 ? (max_seq_len + partition_tokens - 1) / partition_tokens : 1;
+  // keys [L - window, L) touch at most ceil(window / PT) + 1 partitions
+  const long span = ((long)window + partition_tokens - 1) / partition_tokens + 1;
+  return (int)std::min<long>(all, span);
+}
+
+DecodeWorkspaceLayout decode_workspace_layout_p(int batch, int num_q_heads, int head_dim, int P) {
+  DecodeWorkspaceLayout w{0, 0, 0, 0, 0};
   const size_t rows = (size_t)batch * num_q_heads * P;
   w.max_partitions = P;
   w.o_off = 0;

@@ -49,6 +49,10 @@ struct DecodeWorkspaceLayout {
 };
 DecodeWorkspaceLayout decode_workspace_layout(int batch, int num_q_heads, int head_dim,
                                               int max_seq_len, int partition_tokens);
+// Partition slots per sequence of a windowed split call: its partials are indexed from the
+// partition holding the window's first key, so the slots cover the window, not max_seq_len.
+int decode_window_partitions(int max_seq_len, int window, int partition_tokens);
+DecodeWorkspaceLayout decode_workspace_layout_p(int batch, int num_q_heads, int head_dim, int partitions);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

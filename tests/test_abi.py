@@ -24,7 +24,7 @@ def _declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = pkv.load_library()
     syms = _declared_symbols()
-    assert len(syms) == 21, syms
+    assert len(syms) == 22, syms
     for s in syms:
         assert hasattr(lib, s), f"{s} missing from libpkv.so"
     assert set(syms) == set(pkv._SIGNATURES), "binding and header disagree"
@@ -169,6 +169,25 @@ def test_block_calls_argument_errors():
     assert lib.pkv_swap_blocks(fake, fake, mp, 2, 64, 4, 4, nul) == pkv.E_INVALID_ARGUMENT
     assert lib.pkv_swap_blocks(fake, fake, mp, 2, 0, 8, 8, nul) == pkv.E_INVALID_ARGUMENT
     assert lib.pkv_swap_blocks(nul, nul, nul, 0, 64, 4, 4, nul) == pkv.OK
+
+
+def test_window_workspace_covers_only_the_window():
+    lib = pkv.load_library()
+    al = lambda x: (x + 255) // 256 * 256
+    need = lambda B, Hq, D, P: al(B * Hq * P * D * 4) + 2 * al(B * Hq * P * 4)
+    # explicit partitions: ceil(window / PT) + 1 slots per sequence, never more than max_seq_len's
+    assert lib.pkv_decode_window_workspace_bytes(4, 64, 8, 128, 131072, 8192, 512) == need(4, 64, 128, 17)
+    assert lib.pkv_decode_window_workspace_bytes(4, 64, 8, 128, 131072, 8000, 256) == need(4, 64, 128, 33)
+    assert lib.pkv_decode_window_workspace_bytes(2, 8, 8, 64, 1000, 5000, 512) == need(2, 8, 64, 2)
+    # library choice: planned on min(max_seq_len, window) keys (8192 here: 512-token partitions)
+    assert lib.pkv_decode_window_workspace_bytes(4, 64, 8, 128, 131072, 8192, -1) == need(4, 64, 128, 17)
+    assert pkv.decode_window_workspace_bytes(4, 64, 8, 128, 131072, 8192) == need(4, 64, 128, 17)
+    # a short window, or many (sequence, kv head) groups: the direct path, no workspace
+    assert lib.pkv_decode_window_workspace_bytes(4, 64, 8, 128, 131072, 500, -1) == 0
+    assert lib.pkv_decode_window_workspace_bytes(64, 32, 8, 128, 8192, 4096, -1) == 0
+    # no window: the plain call's figure
+    assert lib.pkv_decode_window_workspace_bytes(4, 64, 8, 128, 131072, 0, -1) == \
+        lib.pkv_decode_workspace_bytes(4, 64, 8, 128, 131072, -1)
 
 
 def test_decode_plan_uses_the_real_maximum():

@@ -177,7 +177,7 @@ def test_split_and_direct_agree():
     assert (la - lb).abs().max() <= 2e-3 and (la - lc).abs().max() <= 2e-3
 
 
-@pytest.mark.parametrize("pt", [32, 1024])
+@pytest.mark.parametrize("pt", [32, 1024, -1])
 @pytest.mark.parametrize("window", [40000, 2000])
 def test_decode_long_multi_partition_window(window, pt):
     """A sliding window over long sequences: with 32-token partitions and 40000 keys visible a wave

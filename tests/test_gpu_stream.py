@@ -23,7 +23,7 @@ WINDOW_SHAPES = [
 
 @pytest.mark.parametrize("case", range(len(WINDOW_SHAPES)))
 @pytest.mark.parametrize("window", [1, 17, 100, 512, 513, 4096])
-@pytest.mark.parametrize("pt", [0, 512])
+@pytest.mark.parametrize("pt", [0, 96, 512, -1])
 def test_window_decode(case, window, pt):
     lens, hq, hkv, d, bs = WINDOW_SHAPES[case]
     di = paged_decode_inputs(5000 + case, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seq_lens=lens,
