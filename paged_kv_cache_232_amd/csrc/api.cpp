@@ -355,7 +355,7 @@ static int check_prefill_common(const void* q, const void* out, const int32_t* q
   *max_qo = 0;
   *total_q = 0;
   *tiles = 0;
-  *tile_rows = pkv::prefill_tile_rows(head_dim);
+  *tile_rows = pkv::prefill_tile_rows(head_dim, num_q_heads / num_kv_heads);
   if (batch == 0) return PKV_OK;
   if (!qo_indptr_h || !qo_indptr) return PKV_E_INVALID_ARGUMENT;
   if (qo_indptr_h[0] != 0) return PKV_E_INVALID_ARGUMENT;

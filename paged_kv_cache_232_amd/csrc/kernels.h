@@ -78,14 +78,14 @@ struct PrefillArgs {
   int max_qo_len;   // host-side maximum of the q lengths
   int total_q;      // rows of q / out
   int64_t total_kv; // rows of k / v (ragged only)
-  int tile_rows;    // q rows of one work item (prefill_tile_rows(head_dim))
+  int tile_rows;    // q rows of one work item (prefill_tile_rows(head_dim, group))
   int64_t tiles;    // (request, q tile) work items, from the host copies
   void* workspace;  // >= prefill_workspace_bytes(tiles) bytes (the device-built schedule)
 };
 
 // q rows of one prefill work item for a head dim; the (request, q tile) work items of a launch;
 // and the workspace its schedule needs (0 when the schedule travels with the launch).
-int prefill_tile_rows(int head_dim);
+int prefill_tile_rows(int head_dim, int group);
 int64_t prefill_tile_count(int batch, const int32_t* qo_indptr_h, int tile_rows);
 size_t prefill_workspace_bytes(int64_t tiles);
 

@@ -8,7 +8,8 @@
 //
 // MI355X design (a dense contraction, so MFMA-bound):
 //   * head_dim <= 128: work-group = 4 waves; tile = 128 query rows of one q head (32 rows per
-//     wave); head_dim 256: 12 waves x 16 rows, a 192-row tile;
+//     wave); head_dim 256: 12 waves x 16 rows over hp q heads of one kv head (hp = gcd(G, 12)),
+//     a tile of 192 / hp rows;
 //   * head_dim <= 128: K and V tiles of BN keys go straight from HBM into LDS with direct-to-LDS
 //     loads (global_load_lds_dwordx4), K two tiles ahead and V one tile ahead in rings of 3 and
 //     2 tiles, their 16-byte units permuted within each row so that the MFMA operand reads are
@@ -133,13 +134,14 @@ struct TileWork {
   int b, qt, q0, qo, kv;
   int64_t kv0;
 };
-template <bool PAGED, int BM>
+template <bool PAGED>
 __device__ __forceinline__ bool resolve_tile(int y, const TileOrder& order,
                                              const uint32_t* __restrict__ order_dev,
                                              const int32_t* __restrict__ qo_indptr,
                                              const int32_t* __restrict__ kv_indptr,
                                              const int32_t* __restrict__ kv_lens, int batch,
-                                             int total_q, int total_kv, int kv_cap, TileWork& t) {
+                                             int total_q, int total_kv, int kv_cap, int BM,
+                                             TileWork& t) {
   // made explicitly wave-uniform: the request's extents then stay scalar, and so do the block-table
   // reads the tile loads address from (a vector table read would wait for every load in flight)
   // two separate reads (a select of the two pointers would make one flat load of a generic
@@ -215,8 +217,8 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   xcd_map(Hq, Hkv, G, xcd_group, xcd_heads, h, y);
   if (y >= n_rows) return;
   TileWork tw;
-  if (!resolve_tile<PAGED, kBM>(y, order, order_dev, qo_indptr, kv_indptr, kv_lens, batch, total_q,
-                                total_kv, max_blocks * BS, tw))
+  if (!resolve_tile<PAGED>(y, order, order_dev, qo_indptr, kv_indptr, kv_lens, batch, total_q,
+                           total_kv, max_blocks * BS, kBM, tw))
     return;
   const int b = tw.b;
   const int kh = h / G;
@@ -468,8 +470,12 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 //   O^T += V^T P^T per 32-key step: the lane's 8 probabilities (keys 4*(l/16) + j and
 //     16 + 4*(l/16) + j of the step) are its B operand as they stand; the A operand takes V^T
 //     with the same key order from two LDS transpose reads.
-// 12 waves x 16 rows = a 192-row q tile; the first 8 waves load and stage the K / V tiles (a
-// 32-key tile is 1024 16-byte units: two per loading thread).
+// 12 waves x 16 rows serve hp q heads of one kv head (hp = gcd(G, 12)) over a q tile of 192 / hp
+// rows: with 16 q / 4 kv heads, four heads over 48 rows. The heads share every K / V tile the work-
+// group stages, the waves' causal extents differ by at most a tile height, and a request's last,
+// partial q tile keeps fewer waves idle than a 192-row tile of one head did (455 -> 421 us on the
+// chunked prefill workload, same box). The first 8 waves load and stage the K / V tiles (a 32-key
+// tile is 1024 16-byte units: two per loading thread).
 constexpr int kP16Waves = 12;
 constexpr int kP16Threads = kP16Waves * kWave;
 constexpr int kP16LoadThreads = 8 * kWave;  // threads that load and stage K / V tiles
@@ -507,38 +513,43 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
                  int negate_q, int xcd_group, int xcd_heads, int n_rows, int bs_shift, int batch,
                  int total_q, int total_kv, const uint32_t* __restrict__ order_dev,
-                 const TileOrder order) {
+                 const TileOrder order, int hp) {
   using C = P16Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
   // buffer j (0/1): K rows at smem + j*BUF, V rows BN*RSE further; the output tile reuses it
 
+  // A work-group takes hp q heads of one kv head (hp = gcd(G, 12)) over 16 * 12 / hp query rows:
+  // wave w serves head hs = w % hp, row block rb = w / hp.
   const int G = Hq / Hkv;
-  int h, y;
-  xcd_map(Hq, Hkv, G, xcd_group, xcd_heads, h, y);
+  const int bm = kP16Waves / hp * 16;  // query rows per work-group
+  int hg, y;
+  xcd_map(Hq / hp, Hkv, G / hp, xcd_group, xcd_heads, hg, y);
   if (y >= n_rows) return;
   TileWork tw;
-  if (!resolve_tile<PAGED, kP16BM>(y, order, order_dev, qo_indptr, kv_indptr, kv_lens, batch,
-                                   total_q, total_kv, max_blocks * BS, tw))
+  if (!resolve_tile<PAGED>(y, order, order_dev, qo_indptr, kv_indptr, kv_lens, batch, total_q,
+                           total_kv, max_blocks * BS, bm, tw))
     return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = hg * hp + w % hp;
+  const int rb = w / hp;
   const int b = tw.b;
-  const int kh = h / G;
+  const int kh = (hg * hp) / G;
   const int q0 = tw.q0;
   const int qo = tw.qo;
   const int kv = tw.kv;
   const int64_t kv0 = tw.kv0;
-  const int m0 = tw.qt * kP16BM;
+  const int m0 = tw.qt * bm;
   const int off = kv - qo;  // row i sits at key position i + off
 
   int kv_end = kv;
-  if (causal) kv_end = min(kv, m0 + kP16BM + off);
+  if (causal) kv_end = min(kv, m0 + bm + off);
   const int n_kt = kv_end > 0 ? (kv_end + C::BN - 1) / C::BN : 0;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qcol = lane & 15;  // query of this lane within the wave
   const int grp = lane >> 4;   // 0..3
-  const int row = m0 + w * 16 + qcol;
+  const int row = m0 + rb * 16 + qcol;
   const bool row_ok = row < qo;
 
   // Q^T operand: lane holds Q[row][32*ks + 8*grp .. +8]
@@ -640,7 +651,7 @@ prefill16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     fetch(C::BN, S1{});
     if constexpr (C::PF > 1) fetch(2 * C::BN, S0{});
   }
-  const int wave_first_row = m0 + w * 16;
+  const int wave_first_row = m0 + rb * 16;
   // tiles past the last key a row of this wave sees are skipped, all of them by a wave whose rows
   // lie past the request's end (the q tile's padding)
   const int wave_last_key =
@@ -774,7 +785,21 @@ static int64_t tile_work(int qo, int64_t kv, int qt, int causal, int bm) {
   return std::max<int64_t>(vis, 0);
 }
 
-int prefill_tile_rows(int head_dim) { return head_dim >= 256 ? kP16BM : kBM; }
+// q heads per work-group of the head_dim-256 form: the largest count that divides both the group
+// size and its 12 waves
+int prefill16_heads(int group) {
+  int a = group, b = kP16Waves;
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+int prefill_tile_rows(int head_dim, int group) {
+  return head_dim >= 256 ? kP16BM / prefill16_heads(group) : kBM;
+}
 
 int64_t prefill_tile_count(int batch, const int32_t* qo_indptr_h, int bm) {
   int64_t n = 0;
@@ -919,12 +944,19 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, grid_rows, 1);
   const int bs_shift = a.block_size > 0 ? __builtin_ctz((unsigned)a.block_size) : 0;
   if constexpr (use_p16<D>()) {
-    hipLaunchKernelGGL((prefill16_kernel<D, PAGED>), grid, dim3(kP16Threads), 0, stream,
+    // hp q heads of one kv head per work-group: the XCD mapping runs over head groups
+    const int hp = prefill16_heads(a.num_q_heads / a.num_kv_heads);
+    const int hgs = a.num_q_heads / hp;
+    const bool g8 = hgs % 8 == 0;
+    const int xg = (g8 && 8 % a.num_kv_heads == 0) ? 8 / a.num_kv_heads : 0;
+    const int xh = (g8 && xg == 0) ? hgs / 8 : 0;
+    const int rows16 = xg > 0 ? (n_rows + xg - 1) / xg * xg : n_rows;
+    hipLaunchKernelGGL((prefill16_kernel<D, PAGED>), dim3(hgs, rows16, 1), dim3(kP16Threads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
                        a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
-                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_group, xcd_heads,
-                       n_rows, bs_shift, a.batch, a.total_q, (int)a.total_kv, order_dev, order);
+                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xg, xh, n_rows,
+                       bs_shift, a.batch, a.total_q, (int)a.total_kv, order_dev, order, hp);
   } else {
     hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(kPrefillThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,

@@ -43,8 +43,10 @@ RAGGED_EDGE = [
     ([129, 5, 300], None, 8, 1, 128, True),         # group of 8 rows, 6 rows used
     ([129, 40, 1], [129, 90, 1], 16, 4, 256, True), # group of 2 rows, 4 rows, head_dim 256
     ([1] * 801, [37] * 801, 8, 2, 128, True),       # device-built schedule, groups of 4 rows
-    ([1] * 790, [50] * 790, 4, 2, 256, True),       # device-built schedule of 192-row q tiles
-    ([400, 193, 192, 1], [600, 193, 300, 9], 8, 2, 256, True),  # 192-row q tiles and their edges
+    ([1] * 790, [50] * 790, 4, 2, 256, True),       # device-built schedule, 2 heads x 96-row q tiles
+    ([400, 193, 192, 1], [600, 193, 300, 9], 8, 2, 256, True),  # 4 heads x 48-row q tiles, edges
+    ([250, 97, 1], [400, 97, 30], 3, 3, 256, True), # one head per work-group: 192-row q tiles
+    ([130, 61], [130, 200], 12, 2, 256, True),      # G = 6: 6 heads x 32-row q tiles
 ]
 
 
