@@ -204,7 +204,9 @@ int pkv_paged_attn_decode_noalloc(const void* q, const void* k_cache, const void
  *                when that is 0), 16-byte aligned; it holds the work-group schedule the library
  *                builds on the device. Its contents need no initialisation. Calls that share a
  *                workspace must be ordered (one stream).
- * The work of a launch is cut into (request, 128-row q tile) items run longest-first.
+ * The work of a launch is cut into (request, q tile) items run longest-first; a q tile is
+ * 128 / gcd(G, 4) rows for head_dim <= 128 and 192 / gcd(G, 12) rows for head_dim 256, where
+ * G = num_q_heads / num_kv_heads (one work-group serves that many q heads of one kv head).
  * PKV_E_UNSUPPORTED for head_dim other than 64/128/256, num_kv_heads * head_dim >= 2^23, batch >
  * 65535, a request of more than 65535 q tiles, or more than 65528 q tiles in all (also for
  * pkv_paged_prefill). PKV_E_WORKSPACE_TOO_SMALL when workspace_bytes is below the size above.

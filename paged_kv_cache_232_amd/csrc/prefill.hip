@@ -7,9 +7,10 @@
 // vLLM-derived paged_attn.py page (_forward_prefix_pytorch: cached prefix unmasked, chunk causal).
 //
 // MI355X design (a dense contraction, so MFMA-bound):
-//   * head_dim <= 128: work-group = 4 waves; tile = 128 query rows of one q head (32 rows per
-//     wave); head_dim 256: 12 waves x 16 rows over hp q heads of one kv head (hp = gcd(G, 12)),
-//     a tile of 192 / hp rows;
+//   * head_dim <= 128: work-group = 4 waves x 32 rows over hp q heads of one kv head
+//     (hp = gcd(G, 4)), a tile of 128 / hp rows; head_dim 256: 12 waves x 16 rows over
+//     hp = gcd(G, 12) heads, a tile of 192 / hp rows. The heads of a work-group share each staged
+//     K / V tile, and all its waves see the same causal extent;
 //   * head_dim <= 128: K and V tiles of BN keys go straight from HBM into LDS with direct-to-LDS
 //     loads (global_load_lds_dwordx4), K two tiles ahead and V one tile ahead in rings of 3 and
 //     2 tiles, their 16-byte units permuted within each row so that the MFMA operand reads are
@@ -207,39 +208,44 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                int Hq, int Hkv, int BS, int NB, int max_blocks, int causal, float scale_log2,
                int negate_q, int xcd_group, int xcd_heads, int n_rows, int bs_shift, int batch,
                int total_q, int total_kv, const uint32_t* __restrict__ order_dev,
-               const TileOrder order) {
+               const TileOrder order, int hp) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
   // K ring at smem + j * TILE (j < 3), V ring after it; the output tile reuses the space
 
+  // A work-group takes hp q heads of one kv head (hp = gcd(G, 4)) over 32 * 4 / hp query rows:
+  // wave w serves head hs = w % hp, row block rb = w / hp.
   const int G = Hq / Hkv;
-  int h, y;
-  xcd_map(Hq, Hkv, G, xcd_group, xcd_heads, h, y);
+  const int bm = kPrefillWaves / hp * 32;  // query rows per work-group
+  int hg, y;
+  xcd_map(Hq / hp, Hkv, G / hp, xcd_group, xcd_heads, hg, y);
   if (y >= n_rows) return;
   TileWork tw;
   if (!resolve_tile<PAGED>(y, order, order_dev, qo_indptr, kv_indptr, kv_lens, batch, total_q,
-                           total_kv, max_blocks * BS, kBM, tw))
+                           total_kv, max_blocks * BS, bm, tw))
     return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = hg * hp + w % hp;
+  const int rb = w / hp;
   const int b = tw.b;
-  const int kh = h / G;
+  const int kh = (hg * hp) / G;
   const int q0 = tw.q0;
   const int qo = tw.qo;
   const int kv = tw.kv;
   const int64_t kv0 = tw.kv0;
-  const int m0 = tw.qt * kBM;
+  const int m0 = tw.qt * bm;
   const int off = kv - qo;  // row i sits at key position i + off
 
   // keys this tile can see: [0, kv_end)
   int kv_end = kv;
-  if (causal) kv_end = min(kv, m0 + kBM + off);
+  if (causal) kv_end = min(kv, m0 + bm + off);
   const int n_kt = kv_end > 0 ? (kv_end + C::BN - 1) / C::BN : 0;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
   const int qcol = lane & 31;   // query column of this lane
   const int half = lane >> 5;   // 0/1
-  const int row = m0 + w * 32 + qcol;     // query row within the request
+  const int row = m0 + rb * 32 + qcol;     // query row within the request
   const bool row_ok = row < qo;
 
   // Q^T operand: lane holds Q[row][ks*16 + 8*half .. +8] (loaded after the first tiles, below)
@@ -347,7 +353,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
   // last key any row of this wave can see (causal): tiles past it are skipped by the wave; a wave
   // whose rows all lie past the request's end (the q tile's padding) skips every tile
-  const int wave_last_key = m0 + w * 32 >= qo ? -1 : (causal ? m0 + w * 32 + 31 + off : 0x7fffffff);
+  const int wave_last_key = m0 + rb * 32 >= qo ? -1 : (causal ? m0 + rb * 32 + 31 + off : 0x7fffffff);
   int ks_slot = 0;  // t % 3
   for (int t = 0; t < n_kt; ++t) {
     const int n0 = t * C::BN;
@@ -379,7 +385,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     sched_qk_pipeline<C::KS * C::MT, kQkAhead>();
 
     // mask only tiles crossing the ragged end or this wave's causal diagonal
-    const bool need_mask = (n0 + C::BN > kv) || (causal && n0 + C::BN - 1 > m0 + w * 32 + off);
+    const bool need_mask = (n0 + C::BN > kv) || (causal && n0 + C::BN - 1 > m0 + rb * 32 + off);
     if (need_mask) {
       // key n0 + mt*32 + 8*(r/4) + 4*half + r%4 is visible iff mt*32 + 8*(r/4) + r%4 <= thr
       const int thr = lim - n0 - 4 * half;
@@ -451,7 +457,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int u = lane; u < 32 * C::UPR; u += kWave) {
     const int rr = u / C::UPR;
     const int cu = u - rr * C::UPR;
-    const int orow = m0 + w * 32 + rr;
+    const int orow = m0 + rb * 32 + rr;
     if (orow < qo)
       store16_nt(out + ((size_t)(q0 + orow) * Hq + h) * D + cu * 8,
               *reinterpret_cast<const u32x4*>(ost + rr * C::RSO + cu * 8));
@@ -797,8 +803,12 @@ int prefill16_heads(int group) {
   return a;
 }
 
+// q heads per work-group of the head_dim <= 128 form: the largest count dividing the group size
+// and its 4 waves
+int prefill_heads(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
+
 int prefill_tile_rows(int head_dim, int group) {
-  return head_dim >= 256 ? kP16BM / prefill16_heads(group) : kBM;
+  return head_dim >= 256 ? kP16BM / prefill16_heads(group) : kBM / prefill_heads(group);
 }
 
 int64_t prefill_tile_count(int batch, const int32_t* qo_indptr_h, int bm) {
@@ -932,38 +942,35 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     order_dev = (const uint32_t*)a.workspace;
   }
-  const bool q8 = a.num_q_heads % 8 == 0;
-  const int xcd_group = (q8 && 8 % a.num_kv_heads == 0) ? 8 / a.num_kv_heads : 0;
-  const int xcd_heads = (q8 && xcd_group == 0) ? a.num_q_heads / 8 : 0;
+  // hp q heads of one kv head per work-group; the XCD mapping runs over the Hq / hp head groups
+  const int hp = use_p16<D>() ? prefill16_heads(a.num_q_heads / a.num_kv_heads)
+                              : prefill_heads(a.num_q_heads / a.num_kv_heads);
+  const int hgs = a.num_q_heads / hp;
+  const bool g8 = hgs % 8 == 0;
+  const int xcd_group = (g8 && 8 % a.num_kv_heads == 0) ? 8 / a.num_kv_heads : 0;
+  const int xcd_heads = (g8 && xcd_group == 0) ? hgs / 8 : 0;
   const int n_rows = (int)a.tiles;
   const int grid_rows = xcd_group > 0 ? (n_rows + xcd_group - 1) / xcd_group * xcd_group : n_rows;
   float scale_log2 = a.scale * kLog2e;
   const int negate_q = scale_log2 < 0.f;
   if (negate_q) scale_log2 = -scale_log2;
   if (!(scale_log2 >= 1.17549435e-38f)) scale_log2 = 1.17549435e-38f;  // zero (or denormal) scale
-  const dim3 grid(a.num_q_heads, grid_rows, 1);
+  const dim3 grid(hgs, grid_rows, 1);
   const int bs_shift = a.block_size > 0 ? __builtin_ctz((unsigned)a.block_size) : 0;
   if constexpr (use_p16<D>()) {
-    // hp q heads of one kv head per work-group: the XCD mapping runs over head groups
-    const int hp = prefill16_heads(a.num_q_heads / a.num_kv_heads);
-    const int hgs = a.num_q_heads / hp;
-    const bool g8 = hgs % 8 == 0;
-    const int xg = (g8 && 8 % a.num_kv_heads == 0) ? 8 / a.num_kv_heads : 0;
-    const int xh = (g8 && xg == 0) ? hgs / 8 : 0;
-    const int rows16 = xg > 0 ? (n_rows + xg - 1) / xg * xg : n_rows;
-    hipLaunchKernelGGL((prefill16_kernel<D, PAGED>), dim3(hgs, rows16, 1), dim3(kP16Threads), 0, stream,
+    hipLaunchKernelGGL((prefill16_kernel<D, PAGED>), grid, dim3(kP16Threads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
                        a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
-                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xg, xh, n_rows,
-                       bs_shift, a.batch, a.total_q, (int)a.total_kv, order_dev, order, hp);
+                       a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_group, xcd_heads,
+                       n_rows, bs_shift, a.batch, a.total_q, (int)a.total_kv, order_dev, order, hp);
   } else {
     hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(kPrefillThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.out, a.qo_indptr, a.kv_indptr, a.kv_lens, a.block_tables,
                        a.num_q_heads, a.num_kv_heads, a.block_size, a.num_blocks,
                        a.max_blocks_per_seq, a.causal, scale_log2, negate_q, xcd_group, xcd_heads,
-                       n_rows, bs_shift, a.batch, a.total_q, (int)a.total_kv, order_dev, order);
+                       n_rows, bs_shift, a.batch, a.total_q, (int)a.total_kv, order_dev, order, hp);
   }
   return hipGetLastError();
 }

@@ -96,16 +96,23 @@ def _indptr(lens):
 
 
 def test_prefill_workspace_bytes_and_errors():
-    """Up to 768 (request, 128-row q tile) items the schedule travels with the launch (no workspace);
-    beyond, one 32-bit entry per item, 256-byte aligned. Too small a workspace is reported before any
-    launch; so are schedules the grid cannot hold."""
+    """Up to 768 (request, q tile) items the schedule travels with the launch (no workspace);
+    beyond, one 32-bit entry per item, 256-byte aligned. A q tile is 128 / gcd(G, 4) rows at
+    head_dim <= 128 and 192 / gcd(G, 12) at head_dim 256 (G q heads per kv head). Too small a
+    workspace is reported before any launch; so are schedules the grid cannot hold."""
     lib = pkv.load_library()
     nul = None
     fake = ctypes.c_void_p(1 << 20)
-    small = _indptr([128] * 768)                      # 768 tiles
+    small = _indptr([32] * 768)                       # 768 tiles of 32 rows (G = 4)
     assert pkv.prefill_workspace_bytes(small, 32, 8, 128) == 0
-    big = _indptr([1] * 800 + [129])                  # 802 tiles
+    big = _indptr([1] * 800 + [33])                   # 802 tiles
     assert pkv.prefill_workspace_bytes(big, 32, 8, 128) == (802 * 4 + 255) // 256 * 256
+    # tile heights by group size: G = 1 -> 128 rows, G = 2 -> 64, G = 6 -> 64 (head_dim <= 128);
+    # head_dim 256: G = 4 -> 48, G = 3 -> 64, G = 1 -> 192
+    for hq, hkv, d, rows in [(8, 8, 64, 128), (8, 4, 128, 64), (12, 2, 128, 64), (16, 4, 256, 48),
+                             (6, 2, 256, 64), (4, 4, 256, 192)]:
+        assert pkv.prefill_workspace_bytes(_indptr([rows] * 768), hq, hkv, d) == 0, (hq, hkv, d)
+        assert pkv.prefill_workspace_bytes(_indptr([rows] * 768 + [1]), hq, hkv, d) == 3328, (hq, hkv, d)
     # arguments the calls reject size nothing
     assert pkv.prefill_workspace_bytes(big, 32, 8, 96) == 0
     assert pkv.prefill_workspace_bytes(_indptr([]), 32, 8, 128) == 0
@@ -122,7 +129,7 @@ def test_prefill_workspace_bytes_and_errors():
     assert lib.pkv_paged_prefill(fake, fake, fake, fake, fake, fake, bp, kl.ctypes.data_as(ctypes.c_void_p), fake,
                                  B, 8, 2, 128, 16, 64, 4, 1, 1.0, fake, need - 1, nul) == pkv.E_WORKSPACE_TOO_SMALL
     # more q tiles than one launch's grid holds, and more than 65535 requests
-    huge = _indptr([128 * 1000] * 66)                 # 66000 tiles
+    huge = _indptr([32 * 1000] * 66)                  # 66000 tiles of 32 rows
     hp = huge.ctypes.data_as(ctypes.c_void_p)
     assert lib.pkv_ragged_prefill(fake, fake, fake, fake, fake, fake, hp, hp, 66, 8, 2, 128, 1, 1.0, fake,
                                   1 << 30, nul) == pkv.E_UNSUPPORTED

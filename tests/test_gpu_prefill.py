@@ -22,7 +22,7 @@ def _ragged(ri):
 RAGGED_EDGE = [
     # qo_lens, kv_lens (None = same), Hq, Hkv, D, causal
     ([1], None, 1, 1, 64, True),
-    ([5, 128, 129, 300], None, 4, 2, 128, True),
+    ([5, 128, 129, 300], None, 4, 2, 128, True),   # G = 2: 2 heads x 64-row q tiles
     ([127, 1, 256], None, 8, 1, 64, True),
     ([200, 3], [450, 3], 4, 4, 128, True),          # qo < kv: bottom-right causal offset
     ([70, 9], [40, 9], 2, 1, 128, True),            # qo > kv: leading rows see no key
@@ -30,7 +30,7 @@ RAGGED_EDGE = [
     ([257, 64], None, 16, 4, 256, True),            # head_dim 256
     ([40, 0, 77], [60, 5, 77], 8, 2, 128, True),    # an empty request
     ([300], [0], 2, 1, 64, False),                  # no keys at all
-    ([513, 255, 256], None, 4, 1, 128, True),       # several 256-row q tiles, ragged tails
+    ([513, 255, 256], None, 4, 1, 128, True),       # 4 heads x 32-row q tiles, ragged tails
     ([700, 31], [1500, 31], 2, 2, 64, True),        # long prefix offset, head_dim 64
     ([600, 90], [600, 4000], 4, 2, 128, False),     # non-causal, kv much longer than q
     ([1] * 800, [37] * 800, 2, 1, 64, True),         # more q tiles than the launch arguments hold:
@@ -42,11 +42,16 @@ RAGGED_EDGE = [
     ([200, 17], None, 24, 3, 64, True),             # Hkv = 3: per-XCD heads, head_dim 64
     ([129, 5, 300], None, 8, 1, 128, True),         # group of 8 rows, 6 rows used
     ([129, 40, 1], [129, 90, 1], 16, 4, 256, True), # group of 2 rows, 4 rows, head_dim 256
-    ([1] * 801, [37] * 801, 8, 2, 128, True),       # device-built schedule, groups of 4 rows
+    ([1] * 801, [37] * 801, 8, 2, 128, True),       # device-built schedule, 4 heads x 32 rows
     ([1] * 790, [50] * 790, 4, 2, 256, True),       # device-built schedule, 2 heads x 96-row q tiles
     ([400, 193, 192, 1], [600, 193, 300, 9], 8, 2, 256, True),  # 4 heads x 48-row q tiles, edges
     ([250, 97, 1], [400, 97, 30], 3, 3, 256, True), # one head per work-group: 192-row q tiles
     ([130, 61], [130, 200], 12, 2, 256, True),      # G = 6: 6 heads x 32-row q tiles
+    # head_dim <= 128: a work-group takes gcd(G, 4) heads of one kv head over 128 / that rows
+    ([129, 40, 1, 65], [129, 90, 1, 300], 32, 4, 128, True),  # G = 8: two head groups per kv
+                                                    # head, XCD groups of 2 schedule rows
+    ([100, 64, 65], [100, 64, 200], 12, 2, 64, True),  # G = 6: 2 heads x 64-row q tiles
+    ([97, 33], [97, 150], 6, 2, 128, False),        # G = 3: one head, 128-row q tiles
 ]
 
 
@@ -103,6 +108,8 @@ PAGED_EDGE = [
     ([9, 200, 129], [300, 0, 2000], 16, 4, 256, 16, True),  # 5 schedule rows in groups of 2
     ([77, 1, 256], [33, 4000, 16], 8, 1, 64, 16, True),     # groups of 8, head_dim 64
     ([140, 60], [900, 45], 32, 8, 128, 32, True),           # one row per group
+    ([129, 33, 1], [200, 64, 7], 32, 4, 64, 16, True),      # G = 8: 4 heads x 32 rows, XCD
+                                                            # groups of 2 schedule rows
     # blocks larger than a kv tile (64 keys at head_dim <= 128, 32 at 256): a tile's rows sit in
     # one block at an offset, and the last blocks are partly filled
     ([130, 7], [300, 1000], 8, 2, 128, 128, True),
@@ -157,14 +164,14 @@ def test_paged_prefill_with_empty_prefix_equals_ragged():
 
 
 def test_ragged_prefill_device_schedule_many_tiles():
-    """3 000 (request, q tile) items of mixed lengths: the longest-first order is built on the device in
-    the caller's workspace (items of one work bucket land in any order); every row matches the oracle
+    """9 767 (request, 32-row q tile) items of mixed lengths: the longest-first order is built on the device
+    in the caller's workspace (items of one work bucket land in any order); every row matches the oracle
     and a second run (another order inside the buckets) is identical bit for bit."""
     g = torch.Generator().manual_seed(11)
     qo = [int(x) for x in torch.randint(1, 300, (1900,), generator=g)]
     ri = ragged_prefill_inputs(2100, num_q_heads=8, num_kv_heads=2, head_dim=64, qo_lens=qo, causal=True)
     need = pkv.prefill_workspace_bytes(ri.qo_indptr, 8, 2, 64)
-    tiles = sum((n + 127) // 128 for n in qo)
+    tiles = sum((n + 31) // 32 for n in qo)         # G = 4: 4 heads x 32 rows per work-group
     assert tiles > 768 and need >= 4 * tiles
     ref = oracle.ragged_prefill(ri.q, ri.k, ri.v, ri.qo_indptr, ri.kv_indptr, ri.causal, ri.scale)
     ws = torch.full((need,), 0x5A, dtype=torch.uint8, device=DEV)  # contents need no initialisation
