@@ -823,13 +823,28 @@ size_t prefill_workspace_bytes(int64_t tiles) {
   return tiles <= kMaxOrder ? 0 : align256p((size_t)tiles * sizeof(uint32_t));
 }
 
-// Longest-first schedule of the (request, q tile) work-groups from the host copies of the
-// lengths, for launches of at most kMaxOrder tiles (passed by value with the launch).
-static void build_order(const PrefillArgs& a, TileOrder& ord) {
+// Schedule of the (request, q tile) work-groups from the host copies of the lengths, for launches
+// of at most kMaxOrder tiles (passed by value with the launch).
+//
+// lists == 1: all tiles longest-first. lists > 1: rows y and y' run their head groups on the same
+// XCDs iff y == y' (mod lists) (the XCD mapping of the launch), so each request is kept on one
+// row class: requests are dealt to the classes longest-processing-time first (by their total
+// work), and a class holds its requests in order of their longest tile, each request's tiles
+// together and longest-first. The tiles of one request then run side by side on one XCD and walk
+// the same K/V prefix through its L2 instead of fetching it again from HBM. Classes are
+// interleaved row by row and padded with kNoTile to equal length; if that padding would overflow
+// the by-value list, the plain longest-first order is used.
+static void build_order(const PrefillArgs& a, int lists, TileOrder& ord) {
   struct Item {
     int64_t work;
     uint32_t e;
   };
+  struct Req {
+    int64_t total = 0, longest = 0;
+    int b = 0;
+    std::vector<Item> tiles;
+  };
+  std::vector<Req> reqs;
   std::vector<Item> items;
   for (int b = 0; b < a.batch; ++b) {
     const int qo = a.qo_indptr_h[b + 1] - a.qo_indptr_h[b];
@@ -837,13 +852,56 @@ static void build_order(const PrefillArgs& a, TileOrder& ord) {
                                      : std::min<int64_t>(std::max(a.kv_lens_h[b], 0),
                                                          (int64_t)a.max_blocks_per_seq * a.block_size);
     const int n_qt = (qo + a.tile_rows - 1) / a.tile_rows;
-    for (int qt = 0; qt < n_qt; ++qt)
-      items.push_back({tile_work(qo, kv, qt, a.causal, a.tile_rows), ((uint32_t)b << 16) | (uint32_t)qt});
+    if (n_qt == 0) continue;
+    Req r;
+    r.b = b;
+    for (int qt = 0; qt < n_qt; ++qt) {
+      const Item it{tile_work(qo, kv, qt, a.causal, a.tile_rows), ((uint32_t)b << 16) | (uint32_t)qt};
+      r.tiles.push_back(it);
+      items.push_back(it);
+      r.total += it.work;
+      r.longest = std::max(r.longest, it.work);
+    }
+    reqs.push_back(std::move(r));
   }
-  std::stable_sort(items.begin(), items.end(),
-                   [](const Item& x, const Item& y) { return x.work > y.work; });
-  for (size_t i = 0; i < items.size(); ++i) ord.e[i] = items[i].e;
-  ord.n = (int)items.size();
+  auto longest_first = [](const Item& x, const Item& y) { return x.work > y.work; };
+  auto plain = [&]() {
+    std::stable_sort(items.begin(), items.end(), longest_first);
+    for (size_t i = 0; i < items.size(); ++i) ord.e[i] = items[i].e;
+    ord.n = (int)items.size();
+  };
+  if (lists <= 1 || (int)reqs.size() < 2) return plain();
+  // deal requests to classes, largest total first, each to the least loaded class
+  std::vector<size_t> by_total(reqs.size());
+  for (size_t i = 0; i < reqs.size(); ++i) by_total[i] = i;
+  std::stable_sort(by_total.begin(), by_total.end(),
+                   [&](size_t x, size_t y) { return reqs[x].total > reqs[y].total; });
+  std::vector<int64_t> load(lists, 0);
+  std::vector<std::vector<size_t>> cls(lists);
+  for (size_t i : by_total) {
+    const int c = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[c] += reqs[i].total;
+    cls[c].push_back(i);
+  }
+  size_t len = 0;
+  for (auto& c : cls) {
+    std::stable_sort(c.begin(), c.end(),
+                     [&](size_t x, size_t y) { return reqs[x].longest > reqs[y].longest; });
+    size_t n = 0;
+    for (size_t i : c) n += reqs[i].tiles.size();
+    len = std::max(len, n);
+  }
+  if (len * lists > (size_t)kMaxOrder) return plain();
+  for (int c = 0; c < lists; ++c) {
+    size_t j = 0;
+    for (size_t i : cls[c]) {
+      std::vector<Item>& t = reqs[i].tiles;
+      std::stable_sort(t.begin(), t.end(), longest_first);
+      for (const Item& it : t) ord.e[(j++) * lists + c] = it.e;
+    }
+    for (; j < len; ++j) ord.e[j * lists + c] = kNoTile;
+  }
+  ord.n = (int)(len * lists);
 }
 
 // Device-built longest-first schedule for launches of more tiles than the by-value list holds:
@@ -928,12 +986,25 @@ prefill_plan_kernel(const int32_t* __restrict__ qo_indptr, const int32_t* __rest
 template <int D, bool PAGED>
 static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
   if (a.tiles == 0) return hipSuccess;
+  // hp q heads of one kv head per work-group; the XCD mapping runs over the Hq / hp head groups
+  const int hp = use_p16<D>() ? prefill16_heads(a.num_q_heads / a.num_kv_heads)
+                              : prefill_heads(a.num_q_heads / a.num_kv_heads);
+  const int hgs = a.num_q_heads / hp;
+  const bool g8 = hgs % 8 == 0;
+  const int xcd_group = (g8 && 8 % a.num_kv_heads == 0) ? 8 / a.num_kv_heads : 0;
+  const int xcd_heads = (g8 && xcd_group == 0) ? hgs / 8 : 0;
+  // rows whose head groups share XCDs: y mod row_classes (grouped mapping: the rows of a group;
+  // plain mapping with hgs dividing 8: linear id y * hgs + x puts row y on XCDs (y % (8 / hgs)) *
+  // hgs + x)
+  const int row_classes = xcd_group > 0 ? xcd_group : ((!g8 && 8 % hgs == 0) ? 8 / hgs : 1);
   TileOrder order;
   order.n = 0;
   const uint32_t* order_dev = nullptr;
   const int kv_cap = PAGED ? a.max_blocks_per_seq * a.block_size : 0;
+  int n_rows = (int)a.tiles;
   if (a.tiles <= kMaxOrder) {
-    build_order(a, order);
+    build_order(a, row_classes, order);
+    n_rows = order.n;
   } else {
     hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.qo_indptr,
                        a.kv_indptr, a.kv_lens, a.batch, a.causal, a.total_q, (int)a.total_kv, kv_cap,
@@ -942,14 +1013,6 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     order_dev = (const uint32_t*)a.workspace;
   }
-  // hp q heads of one kv head per work-group; the XCD mapping runs over the Hq / hp head groups
-  const int hp = use_p16<D>() ? prefill16_heads(a.num_q_heads / a.num_kv_heads)
-                              : prefill_heads(a.num_q_heads / a.num_kv_heads);
-  const int hgs = a.num_q_heads / hp;
-  const bool g8 = hgs % 8 == 0;
-  const int xcd_group = (g8 && 8 % a.num_kv_heads == 0) ? 8 / a.num_kv_heads : 0;
-  const int xcd_heads = (g8 && xcd_group == 0) ? hgs / 8 : 0;
-  const int n_rows = (int)a.tiles;
   const int grid_rows = xcd_group > 0 ? (n_rows + xcd_group - 1) / xcd_group * xcd_group : n_rows;
   float scale_log2 = a.scale * kLog2e;
   const int negate_q = scale_log2 < 0.f;

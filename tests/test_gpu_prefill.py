@@ -52,6 +52,11 @@ RAGGED_EDGE = [
                                                     # head, XCD groups of 2 schedule rows
     ([100, 64, 65], [100, 64, 200], 12, 2, 64, True),  # G = 6: 2 heads x 64-row q tiles
     ([97, 33], [97, 150], 6, 2, 128, False),        # G = 3: one head, 128-row q tiles
+    # schedules kept per XCD row class (a request's tiles on one XCD): 8 classes at 4 / 1 heads; a
+    # request of 100 tiles would pad the class lists past the by-value schedule, so the plain
+    # longest-first order runs instead
+    ([3200, 40, 7], None, 4, 1, 64, True),
+    ([300, 290, 40, 7, 100], [900, 290, 40, 60, 100], 8, 1, 64, True),  # 2 head groups, 4 classes
 ]
 
 
