@@ -58,17 +58,17 @@ METRIC = "decode KV GB/s (% HBM peak); ragged-prefill bf16 TFLOP/s (% MFMA peak)
 # mismatch reports traffic as null.
 CSRC = os.path.join(ROOT, "paged_kv_cache_232_amd", "csrc")
 TRAFFIC = {
-    "scatter5": (("cache.hip",), "ca92b19357222b29", 71236686),
-    "paged5": (("prefill.hip", "common.h"), "0859a4eb6f7cea2f", 513636923),
-    "ragged2": (("prefill.hip", "common.h"), "0859a4eb6f7cea2f", 194230885),
+    "scatter5": (("cache.hip",), "ca92b19357222b29", 71236688),
+    "paged5": (("prefill.hip", "common.h"), "a0554430c2e6d609", 389290091),
+    "ragged2": (("prefill.hip", "common.h"), "a0554430c2e6d609", 194126872),
     # calls whose path the library chooses: the planner's source counts too
-    "decode3": (("decode.hip", "common.h", "api.cpp"), "7dd64f6e80fb6a17", 1019096621),
-    "decode3_direct": (("decode.hip", "common.h"), "087d5755d82003db", 1019096621),
-    "decode3_split": (("decode.hip", "common.h"), "087d5755d82003db", 1039522714),
-    "decode4": (("decode.hip", "common.h"), "087d5755d82003db", 2220429043),
-    "decode3_fp8": (("decode.hip", "common.h", "api.cpp"), "7dd64f6e80fb6a17", 510453934),
-    "decode4_fp8": (("decode.hip", "common.h", "api.cpp"), "7dd64f6e80fb6a17", 1083850347),
-    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073882832),
+    "decode3": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 1019097671),
+    "decode3_direct": (("decode.hip", "common.h"), "323c2aaa61f82093", 1019097671),
+    "decode3_split": (("decode.hip", "common.h"), "323c2aaa61f82093", 1039527371),
+    "decode4": (("decode.hip", "common.h"), "323c2aaa61f82093", 2220461163),
+    "decode3_fp8": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 510439217),
+    "decode4_fp8": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 1083837289),
+    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073892866),
 }
 
 
