@@ -149,6 +149,8 @@ def build_cases(dev, tune=True):
               qi=ci.qo_indptr.to(dev), kl=ci.kv_lens.to(dev), qi_h=ci.qo_indptr, kl_h=ci.kv_lens,
               scale=ci.scale)
     c5["out"] = torch.empty_like(c5["q"])
+    c5["ws"] = torch.empty(max(pkv.prefill_workspace_bytes(ci.qo_indptr, spec["num_q_heads"], spec["num_kv_heads"],
+                                                           spec["head_dim"]), 16), dtype=torch.uint8, device=dev)
     T5 = int(ci.qo_indptr[-1])
     chunk = [int(ci.qo_indptr[b + 1] - ci.qo_indptr[b]) for b in range(len(ci.kv_lens))]
     kvl5 = ci.kv_lens.tolist()
@@ -159,7 +161,7 @@ def build_cases(dev, tune=True):
     cases["paged5"] = Case(
         "paged_prefill (16 req, prefix U[0,4096], chunk U[64,1024], 16/4 heads, hd 256)",
         lambda: pkv.paged_prefill(c5["q"], c5["kc"], c5["vc"], c5["bt"], c5["qi"], c5["kl"], True, c5["scale"],
-                                  qo_indptr_h=c5["qi_h"], kv_lens_h=c5["kl_h"], out=c5["out"]),
+                                  qo_indptr_h=c5["qi_h"], kv_lens_h=c5["kl_h"], out=c5["out"], workspace=c5["ws"]),
         "mfma", prefill_flops(chunk, kvl5, spec["num_q_heads"], spec["head_dim"], True), "TFLOP/s",
         {"q_tokens_per_s": T5})
     meta = {"T5": T5, "prefix_mean": float(ci.prefix_lens.float().mean()), "chunk_mean": T5 / len(chunk)}
@@ -171,11 +173,13 @@ def build_cases(dev, tune=True):
     c2 = dict(q=ri.q.to(dev), k=ri.k.to(dev), v=ri.v.to(dev), qi=ri.qo_indptr.to(dev), ki=ri.kv_indptr.to(dev),
               qi_h=ri.qo_indptr, ki_h=ri.kv_indptr, scale=ri.scale)
     c2["out"] = torch.empty_like(c2["q"])
+    c2["ws"] = torch.empty(max(pkv.prefill_workspace_bytes(ri.qo_indptr, spec["num_q_heads"], spec["num_kv_heads"],
+                                                           spec["head_dim"]), 16), dtype=torch.uint8, device=dev)
     lens2 = [int(ri.qo_indptr[b + 1] - ri.qo_indptr[b]) for b in range(8)]
     cases["ragged2"] = Case(
         "ragged_prefill (8 req, U[128,2048], 32/8 heads, hd 128, causal)",
         lambda: pkv.ragged_prefill(c2["q"], c2["k"], c2["v"], c2["qi"], c2["ki"], True, c2["scale"],
-                                   qo_indptr_h=c2["qi_h"], kv_indptr_h=c2["ki_h"], out=c2["out"]),
+                                   qo_indptr_h=c2["qi_h"], kv_indptr_h=c2["ki_h"], out=c2["out"], workspace=c2["ws"]),
         "mfma", prefill_flops(lens2, lens2, spec["num_q_heads"], spec["head_dim"], True), "TFLOP/s",
         {"q_tokens_per_s": sum(lens2)})
     meta["lens2"] = lens2
