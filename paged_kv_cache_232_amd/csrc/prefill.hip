@@ -830,10 +830,12 @@ size_t prefill_workspace_bytes(int64_t tiles) {
 // XCDs iff y == y' (mod lists) (the XCD mapping of the launch), so each request is kept on one
 // row class: requests are dealt to the classes longest-processing-time first (by their total
 // work), and a class holds its requests in order of their longest tile, each request's tiles
-// together and longest-first. The tiles of one request then run side by side on one XCD and walk
-// the same K/V prefix through its L2 instead of fetching it again from HBM. Classes are
-// interleaved row by row and padded with kNoTile to equal length; if that padding would overflow
-// the by-value list, the plain longest-first order is used.
+// together and shortest-first. The tiles of one request then run side by side on one XCD and walk
+// the same K/V prefix through its L2 instead of fetching it again from HBM. (Shortest-first within
+// a request: the chunked prefill workload read 290 MB per call against 321 MB longest-first, in
+// the same time; ordering the requests by total work or by tile count ran 5-13 % slower.) Classes
+// are interleaved row by row and padded with kNoTile to equal length; if that padding would
+// overflow the by-value list, the plain longest-first order is used.
 static void build_order(const PrefillArgs& a, int lists, TileOrder& ord) {
   struct Item {
     int64_t work;
@@ -896,7 +898,8 @@ static void build_order(const PrefillArgs& a, int lists, TileOrder& ord) {
     size_t j = 0;
     for (size_t i : cls[c]) {
       std::vector<Item>& t = reqs[i].tiles;
-      std::stable_sort(t.begin(), t.end(), longest_first);
+      std::stable_sort(t.begin(), t.end(),
+                       [](const Item& x, const Item& y) { return x.work < y.work; });
       for (const Item& it : t) ord.e[(j++) * lists + c] = it.e;
     }
     for (; j < len; ++j) ord.e[j * lists + c] = kNoTile;
