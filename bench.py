@@ -58,17 +58,17 @@ METRIC = "decode KV GB/s (% HBM peak); ragged-prefill bf16 TFLOP/s (% MFMA peak)
 # mismatch reports traffic as null.
 CSRC = os.path.join(ROOT, "paged_kv_cache_232_amd", "csrc")
 TRAFFIC = {
-    "scatter5": (("cache.hip",), "ca92b19357222b29", 71236688),
-    "paged5": (("prefill.hip", "common.h"), "a0554430c2e6d609", 389290091),
-    "ragged2": (("prefill.hip", "common.h"), "a0554430c2e6d609", 194126872),
+    "scatter5": (("cache.hip",), "ca92b19357222b29", 71237246),
+    "paged5": (("prefill.hip", "common.h"), "db6cadbe9847c3ef", 359869081),
+    "ragged2": (("prefill.hip", "common.h"), "db6cadbe9847c3ef", 194405831),
     # calls whose path the library chooses: the planner's source counts too
-    "decode3": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 1019097671),
-    "decode3_direct": (("decode.hip", "common.h"), "323c2aaa61f82093", 1019097671),
-    "decode3_split": (("decode.hip", "common.h"), "323c2aaa61f82093", 1039527371),
-    "decode4": (("decode.hip", "common.h"), "323c2aaa61f82093", 2220461163),
-    "decode3_fp8": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 510439217),
-    "decode4_fp8": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 1083837289),
-    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073892866),
+    "decode3": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 1019101249),
+    "decode3_direct": (("decode.hip", "common.h"), "323c2aaa61f82093", 1019101249),
+    "decode3_split": (("decode.hip", "common.h"), "323c2aaa61f82093", 1039513562),
+    "decode4": (("decode.hip", "common.h"), "323c2aaa61f82093", 2220460511),
+    "decode3_fp8": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 510444725),
+    "decode4_fp8": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 1083837297),
+    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073889632),
 }
 
 
