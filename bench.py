@@ -62,12 +62,12 @@ TRAFFIC = {
     "paged5": (("prefill.hip", "common.h"), "db6cadbe9847c3ef", 359869081),
     "ragged2": (("prefill.hip", "common.h"), "db6cadbe9847c3ef", 194405831),
     # calls whose path the library chooses: the planner's source counts too
-    "decode3": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 1019101249),
+    "decode3": (("decode.hip", "common.h", "api.cpp"), "587cfab9b83cc238", 1019101249),
     "decode3_direct": (("decode.hip", "common.h"), "323c2aaa61f82093", 1019101249),
     "decode3_split": (("decode.hip", "common.h"), "323c2aaa61f82093", 1039513562),
     "decode4": (("decode.hip", "common.h"), "323c2aaa61f82093", 2220460511),
-    "decode3_fp8": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 510444725),
-    "decode4_fp8": (("decode.hip", "common.h", "api.cpp"), "78559fd7dba43e9e", 1083837297),
+    "decode3_fp8": (("decode.hip", "common.h", "api.cpp"), "587cfab9b83cc238", 510444725),
+    "decode4_fp8": (("decode.hip", "common.h", "api.cpp"), "587cfab9b83cc238", 1083837297),
     "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073889632),
 }
 

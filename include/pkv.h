@@ -107,7 +107,9 @@ int pkv_decode_plan(const int32_t* seq_lens_h, int32_t batch, int32_t num_q_head
  *   partition_tokens  0 = direct; > 0 = split (a multiple of 32); -1 = library choice: direct
  *                when batch * num_kv_heads * ceil(group / 16) >= 512 or max_seq_len <= 512, else
  *                split with the longest power-of-two partition from 512 to 8192 tokens that still
- *                gives 1024 partitions of (sequence, kv head, 16-head group) at max_seq_len.
+ *                gives 1024 partitions of (sequence, kv head, 16-head group) at max_seq_len; if
+ *                512 tokens give fewer than 384 such partitions, the partition halves (down to
+ *                128 tokens) until they reach 384.
  *   workspace    device scratch of at least pkv_decode_workspace_bytes(...) bytes (may be NULL
  *                when that is 0). Its contents need no initialisation.
  */

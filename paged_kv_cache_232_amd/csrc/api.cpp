@@ -30,11 +30,17 @@ constexpr int64_t kMaxPrefillGridRows = 65528;
 // _PARTITION_SIZE) and doubles while the longest sequence still yields 1024 single-wave
 // partitions (four per CU): one wave then streams a long run of keys with nothing parked in LDS.
 // On 4 x 131072 tokens (64 / 8 heads) that is 4096-token partitions: bf16 335 us against 348 us
-// at 512, an fp8 cache 175 us against 209 us (same box).
+// at 512, an fp8 cache 175 us against 209 us (same box). When 512-token partitions give fewer
+// than 384 waves (a short window over few sequences) the partition halves instead, down to 128
+// tokens, until they reach that: window 2048 over 4 sequences (64 / 8 heads) runs 24.1 us at 128
+// against 32.1 us at 512 (same box), while 4-16-sequence batches of 3000-7000 tokens, with 448 or
+// more waves at 512, ran the same or 2 % slower at 256.
 constexpr int kDefaultPartition = 512;
 constexpr int kMaxAutoPartition = 8192;
+constexpr int kMinAutoPartition = 128;
 constexpr int kDirectMinGroups = 512;  // two (sequence, kv head) work-groups per CU
 constexpr long kSplitMinWaves = 1024;
+constexpr long kSplitFewWaves = 384;
 
 int resolve_partition(int batch, int num_q_heads, int num_kv_heads, int max_seq_len,
                       int partition_tokens) {
@@ -46,6 +52,8 @@ int resolve_partition(int batch, int num_q_heads, int num_kv_heads, int max_seq_
   while (pt < kMaxAutoPartition &&
          groups * (((long)max_seq_len + 2 * pt - 1) / (2 * pt)) >= kSplitMinWaves)
     pt *= 2;
+  while (pt > kMinAutoPartition && groups * (((long)max_seq_len + pt - 1) / pt) < kSplitFewWaves)
+    pt /= 2;
   return pt;
 }
 

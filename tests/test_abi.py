@@ -214,7 +214,10 @@ def test_decode_plan_uses_the_real_maximum():
     assert pkv.decode_plan([131072] * 4, 64, 8, 128)[1] == 4096   # 32 groups x 32 partitions
     assert pkv.decode_plan([131072], 32, 8, 128)[1] == 1024       # 8 groups x 128 partitions
     assert pkv.decode_plan([65536] * 16, 64, 8, 128)[1] == 8192   # capped
-    assert pkv.decode_plan([600], 8, 8, 64)[1] == 512             # too short to fill: the floor
+    # few waves at 512 tokens: the partition halves until 384 waves or 128 tokens
+    assert pkv.decode_plan([600], 8, 8, 64)[1] == 128             # 8 groups: 16 -> 40 waves
+    assert pkv.decode_plan([2048] * 4, 64, 8, 128)[1] == 128      # 32 groups: 128 -> 512 waves
+    assert pkv.decode_plan([7000] * 4, 32, 8, 128)[1] == 512      # 32 groups: 448 waves
     assert pkv.decode_plan([], 32, 8, 128) == (0, 0, 0)
     with pytest.raises(pkv.PkvError):
         pkv.decode_plan([5, -1], 32, 8, 128)
