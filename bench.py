@@ -11,12 +11,13 @@ Each call is bracketed by HIP events on the stream it is launched on. The headli
 decode KV bandwidth (algorithmic bytes of calls 3 and 4 over their measured time); the ragged
 prefill TFLOP/s is reported beside it. The direct and split decode paths of workload 3, decode of
 workloads 3 and 4 over an fp8 (e4m3) cache, a sliding window over workload 4, workload 3 streamed
-over tiles of resident blocks, a small decode step (eager and replayed from a HIP graph), and the
+over tiles of resident blocks, a small decode step and the same step over 32 layers (each eager and
+replayed from a HIP graph), and the
 block-management calls (copy_blocks over 32 layers, swap_blocks to pinned host
 memory) are timed separately, outside the step.
 
 Besides rates and roofline fractions, every call reports tokens per second (decoded sequences and
-KV tokens attended for decode, query rows for prefill); the decode step is also timed host-inclusive
+KV tokens attended for decode, query rows for prefill); the decode steps are also timed host-inclusive
 (wall clock over back-to-back calls), eager and replayed from a graph; a plain 1 GiB device copy is
 timed for context; the batched and long-context decodes also run with a plan measured by
 pkv_decode_tune.
@@ -326,6 +327,30 @@ def build_cases(dev, tune=True):
     cases["decode_step_graph"] = Case("decode step replayed from a HIP graph (same step)", graph.replay, "hbm",
                                       sbytes, "GB/s", stok)
     meta["graph"] = graph  # keep the captured graph alive
+    # the same step over 32 layers, each with its own K/V cache (a model's decode step runs it once
+    # per layer): one graph launch then carries 96 kernels, so its fixed launch cost is shared
+    nl = 32
+    lkc = [ds["kc"].clone() for _ in range(nl)]
+    lvc = [ds["vc"].clone() for _ in range(nl)]
+
+    def layers_step(ds=ds, mx=mx, ptp=ptp):
+        for kc_l, vc_l in zip(lkc, lvc):
+            pkv.reshape_and_cache(ds["kn"], ds["vn"], kc_l, vc_l, ds["slots"])
+            pkv.paged_attn_decode(ds["q"], kc_l, vc_l, ds["bt"], ds["sl"], sd.scale, max_seq_len=mx,
+                                  partition_tokens=ptp, out=ds["out"], workspace=ds["ws"])
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layers_step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph32 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph32):
+        layers_step()
+    ltok = {k: v * nl for k, v in stok.items()}
+    cases["decode_step32_eager"] = Case(f"decode step over {nl} layers, eager launches", layers_step, "hbm",
+                                        sbytes * nl, "GB/s", ltok)
+    cases["decode_step32_graph"] = Case(f"decode step over {nl} layers replayed from one HIP graph",
+                                        graph32.replay, "hbm", sbytes * nl, "GB/s", ltok)
+    meta["graph32"] = (graph32, lkc, lvc)
 
     # block management around the cache (timed alone, outside the step): copy_blocks over 32
     # layers of the batched-decode cache shape, and a swap-out of 256 blocks to pinned host memory
@@ -351,9 +376,10 @@ def build_cases(dev, tune=True):
 STEP = ["scatter5", "paged5", "ragged2", "decode3", "decode4"]
 # timed alone, outside the step
 EXTRA = ["decode3_direct", "decode3_split", "decode3_tuned", "decode4_tuned", "decode3_fp8", "decode4_fp8",
-         "decode4_window", "decode3_streamed", "decode_step_eager", "decode_step_graph", "copy_blocks", "swap_out"]
+         "decode4_window", "decode3_streamed", "decode_step_eager", "decode_step_graph", "decode_step32_eager",
+         "decode_step32_graph", "copy_blocks", "swap_out"]
 # host-inclusive latency (wall clock over many back-to-back calls, then one synchronisation)
-HOST_TIMED = ["decode_step_eager", "decode_step_graph"]
+HOST_TIMED = ["decode_step_eager", "decode_step_graph", "decode_step32_eager", "decode_step32_graph"]
 
 
 def time_step(cases, steps, warmup):
