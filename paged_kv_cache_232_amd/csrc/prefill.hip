@@ -11,10 +11,12 @@
 //     (hp = gcd(G, 4)), a tile of 128 / hp rows; head_dim 256: 12 waves x 16 rows over
 //     hp = gcd(G, 12) heads, a tile of 192 / hp rows. The heads of a work-group share each staged
 //     K / V tile, and all its waves see the same causal extent;
-//   * head_dim <= 128: K and V tiles of BN keys go straight from HBM into LDS with direct-to-LDS
-//     loads (global_load_lds_dwordx4), K two tiles ahead and V one tile ahead in rings of 3 and
+//   * head_dim <= 128: K and V tiles of 32 keys go straight from HBM into LDS with direct-to-LDS
+//     loads (global_load_lds_dwordx4), K three tiles ahead and V one tile ahead in rings of 4 and
 //     2 tiles, their 16-byte units permuted within each row so that the MFMA operand reads are
-//     free of bank conflicts; one explicit wait and barrier per tile;
+//     free of bank conflicts; one explicit wait and barrier per tile. The 32-key tiles keep a
+//     wave at 166 VGPRs and a work-group at 48 KB of LDS, so three work-groups share a CU (three
+//     waves per SIMD); with 64-key tiles two did, and the ragged prefill ran 3-4 % slower;
 //   * head_dim 256 (16-row form below, 12 waves): tiles are loaded into registers a tile ahead and
 //     staged into padded LDS rows (direct-to-LDS loads measured slower there);
 //   * the QK^T MFMAs are scheduled with four LDS reads of K in flight;
@@ -108,7 +110,7 @@ __device__ __forceinline__ int swz(int r) {
 
 template <int D>
 struct PrefillCfg {
-  static constexpr int BN = (D >= 256) ? 32 : 64;   // keys per kv tile
+  static constexpr int BN = 32;                     // keys per kv tile
   static constexpr int KS = D / 16;                 // 16-wide d steps of QK^T
   static constexpr int MT = BN / 32;                // 32-key tiles of S^T
   static constexpr int PS = BN / 16;                // 16-key steps of PV
@@ -118,8 +120,9 @@ struct PrefillCfg {
   static constexpr int ROWS_PER_LOAD = kWave / UPR; // rows one wave load instruction fills
   static constexpr int NL = BN * UPR / (kWave * kPrefillWaves);  // load instructions per wave per tile
   static constexpr int RSO = D + 8;                 // row stride of the staged output tile
-  // K tiles in a ring of 3 (loaded two tiles ahead), V tiles in a ring of 2 (one tile ahead)
-  static constexpr int KBUF = 3, VBUF = 2;
+  // K tiles in a ring of 4 (loaded three tiles ahead), V tiles in a ring of 2 (one tile ahead):
+  // K is needed first in a step, so it gets the longer lead (V two tiles ahead measured slower)
+  static constexpr int KBUF = 4, VBUF = 2;
   static constexpr int LDS_ELEMS =
       ((KBUF + VBUF) * TILE > kBM * RSO) ? (KBUF + VBUF) * TILE : kBM * RSO;
   static_assert(NL * kWave * kPrefillWaves == BN * UPR, "tile units must divide evenly");
@@ -200,7 +203,7 @@ struct PagedLoader {
 // scale_log2 > 0 always: the host folds a negative scale into negate_q (an exact sign flip of q)
 // and replaces a zero scale by the smallest normal float (every score then rounds to 2^0 = 1).
 template <int D, bool PAGED>
-__global__ void __launch_bounds__(kPrefillThreads, 2)
+__global__ void __launch_bounds__(kPrefillThreads, 3)
 prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
                const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr,
@@ -211,7 +214,7 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const TileOrder order, int hp) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
-  // K ring at smem + j * TILE (j < 3), V ring after it; the output tile reuses the space
+  // K ring at smem + j * TILE (j < 4), V ring after it; the output tile reuses the space
 
   // A work-group takes hp q heads of one kv head (hp = gcd(G, 4)) over 32 * 4 / hp query rows:
   // wave w serves head hs = w % hp, row block rb = w / hp.
@@ -331,12 +334,14 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int tr_lo = tr_row * D + 4 * (lane & 1);
   const int tr_hi = (tr_row + 8) * D + 4 * (lane & 1);
 
-  // Pipeline, per wave: issue order K0 V0 K1 | V1 K2 | V2 K3 | ... (step t issues V(t+1) and
-  // K(t+2)); so before step t only K(t+1)'s NL loads may still be in flight.
+  // Pipeline, per wave: issue order K0 V0 K1 K2 | V1 K3 | V2 K4 | ... (step t issues V(t+1) and
+  // K(t+3)); so before step t only K(t+2)'s NL loads may still be in flight (before step 0 also
+  // K1's: waiting for them too is merely early).
   if (n_kt > 0) {
     load_tile(k, 0, k_lds_of(0));
     load_tile(v, 0, v_lds_of(0));
     if (n_kt > 1) load_tile(k, 1, k_lds_of(1));
+    if (n_kt > 2) load_tile(k, 2, k_lds_of(2));
   }
   // q rows are loaded after the first tiles' loads are issued, so those queue first (2-3 % faster
   // on the ragged prefill than the other order)
@@ -354,18 +359,16 @@ prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // last key any row of this wave can see (causal): tiles past it are skipped by the wave; a wave
   // whose rows all lie past the request's end (the q tile's padding) skips every tile
   const int wave_last_key = m0 + rb * 32 >= qo ? -1 : (causal ? m0 + rb * 32 + 31 + off : 0x7fffffff);
-  int ks_slot = 0;  // t % 3
   for (int t = 0; t < n_kt; ++t) {
     const int n0 = t * C::BN;
-    // tile t landed for every wave; every wave is done with tile t-1's buffers
-    if (t + 1 < n_kt) wait_vm_barrier<C::NL>();
+    // tile t landed for every wave; every wave is done with tile t-1's buffers (K(t+3) reuses
+    // K(t-1)'s slot, V(t+1) V(t-1)'s)
+    if (t + 2 < n_kt) wait_vm_barrier<C::NL>();
     else wait_vm_barrier<0>();
-    const int ks_next2 = ks_slot >= 1 ? ks_slot - 1 : 2;  // (t + 2) % 3
     if (t + 1 < n_kt) load_tile(v, t + 1, v_lds_of((t + 1) & 1));
-    if (t + 2 < n_kt) load_tile(k, t + 2, k_lds_of(ks_next2));
-    const uint16_t* const k_lds = smem + ks_slot * C::TILE;
+    if (t + 3 < n_kt) load_tile(k, t + 3, k_lds_of((t + 3) & 3));
+    const uint16_t* const k_lds = smem + (t & 3) * C::TILE;
     const uint16_t* const v_lds = smem + (C::KBUF + (t & 1)) * C::TILE;
-    ks_slot = ks_slot == 2 ? 0 : ks_slot + 1;
     if (n0 > wave_last_key) continue;
 
     // S^T tile: lane holds keys n0 + mt*32 + 8*(r/4) + 4*half + r%4 of query qcol (raw scores)

@@ -115,7 +115,7 @@ PAGED_EDGE = [
     ([140, 60], [900, 45], 32, 8, 128, 32, True),           # one row per group
     ([129, 33, 1], [200, 64, 7], 32, 4, 64, 16, True),      # G = 8: 4 heads x 32 rows, XCD
                                                             # groups of 2 schedule rows
-    # blocks larger than a kv tile (64 keys at head_dim <= 128, 32 at 256): a tile's rows sit in
+    # blocks larger than a kv tile (32 keys): a tile's rows sit in
     # one block at an offset, and the last blocks are partly filled
     ([130, 7], [300, 1000], 8, 2, 128, 128, True),
     ([66, 200], [129, 511], 4, 4, 64, 256, True),
