@@ -59,17 +59,17 @@ METRIC = "decode KV GB/s (% HBM peak); ragged-prefill bf16 TFLOP/s (% MFMA peak)
 # mismatch reports traffic as null.
 CSRC = os.path.join(ROOT, "paged_kv_cache_232_amd", "csrc")
 TRAFFIC = {
-    "scatter5": (("cache.hip",), "ca92b19357222b29", 71237246),
-    "paged5": (("prefill.hip", "common.h"), "db6cadbe9847c3ef", 359869081),
-    "ragged2": (("prefill.hip", "common.h"), "db6cadbe9847c3ef", 194405831),
+    "scatter5": (("cache.hip",), "ca92b19357222b29", 71235247),
+    "paged5": (("prefill.hip", "common.h"), "f49de67e0e090139", 360248764),
+    "ragged2": (("prefill.hip", "common.h"), "f49de67e0e090139", 190617705),
     # calls whose path the library chooses: the planner's source counts too
-    "decode3": (("decode.hip", "common.h", "api.cpp"), "587cfab9b83cc238", 1019101249),
-    "decode3_direct": (("decode.hip", "common.h"), "323c2aaa61f82093", 1019101249),
-    "decode3_split": (("decode.hip", "common.h"), "323c2aaa61f82093", 1039513562),
-    "decode4": (("decode.hip", "common.h"), "323c2aaa61f82093", 2220460511),
-    "decode3_fp8": (("decode.hip", "common.h", "api.cpp"), "587cfab9b83cc238", 510444725),
-    "decode4_fp8": (("decode.hip", "common.h", "api.cpp"), "587cfab9b83cc238", 1083837297),
-    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073889632),
+    "decode3": (("decode.hip", "common.h", "api.cpp"), "587cfab9b83cc238", 1019115770),
+    "decode3_direct": (("decode.hip", "common.h"), "323c2aaa61f82093", 1019115770),
+    "decode3_split": (("decode.hip", "common.h"), "323c2aaa61f82093", 1039502301),
+    "decode4": (("decode.hip", "common.h"), "323c2aaa61f82093", 2220469594),
+    "decode3_fp8": (("decode.hip", "common.h", "api.cpp"), "587cfab9b83cc238", 510425645),
+    "decode4_fp8": (("decode.hip", "common.h", "api.cpp"), "587cfab9b83cc238", 1083848862),
+    "copy_blocks": (("blocks.hip",), "e2f6aca7c6815576", 1073908547),
 }
 
 
