@@ -122,6 +122,8 @@ PAGED_EDGE = [
     ([150, 40], [257, 1500], 16, 4, 256, 128, True),
     ([33, 140], [700, 3], 4, 1, 256, 256, True),
     ([200, 70, 1], [300, 0, 40], 8, 2, 128, 128, True),
+    ([97, 64, 33], [64, 190, 1], 16, 4, 128, 64, True),    # blocks of two kv tiles at head_dim 128
+    ([130, 31], [33, 96], 8, 2, 128, 32, True),            # blocks of exactly one kv tile
     # non-causal: every query row sees the whole prefix and chunk
     ([100, 140], [250, 33], 4, 2, 128, 16, False),
     ([60, 129], [1000, 0], 16, 4, 256, 16, False),
