@@ -514,7 +514,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library's hot path runs on a single MI355X and no "
-              "multi-GPU path is built (see the sharding notes in the design document).", file=sys.stderr)
+              "multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
