@@ -13,7 +13,7 @@ Sources, by page title and section:
              qo_indptr / kv_indptr) and its CPU-reference test (per-request causal GQA attention).
   [libmir]   libmir-cuda 0.3.0 src/backend/kv/attention/mod.rs, ``PagedAttentionBf16::validate_table``.
 
-Readings where the pages leave a step open (each is also listed in the design notes):
+Readings where the pages leave a step open:
   * cache layout is [num_blocks, num_kv_heads, block_size, head_dim] for K and V;
   * block tables are int32 padded with -1; only the first ceil(L/block_size) entries are read;
   * slots past a sequence's length are excluded by length (never read), whatever they hold;

@@ -10,7 +10,7 @@ Source, by page title and section:
             ``k_scale`` / ``v_scale`` floats next to the caches; the page names the arguments but not
             the format or the arithmetic.
 
-Readings where the page leaves the step open (each is also listed in the design notes):
+Readings where the page leaves the step open:
   * format: OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
     exponent field 0 holds subnormals m * 2^-9; S.1111.111 is NaN; there are no infinities and the
     largest finite magnitude is 448;
