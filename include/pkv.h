@@ -20,6 +20,10 @@
  *     numbers, never an out-of-bounds access. pkv_validate_block_tables_h checks tables.
  *   - Slots that hold no token (the tail of a sequence's last block, unused blocks) may hold any
  *     bits, NaN included: they are excluded by length, never read into a result.
+ *   - Calls that read the cache through block tables (decode in every form, paged prefill, the
+ *     streamed decode) need num_blocks >= 1 and max_blocks_per_seq >= 1, even when every sequence
+ *     is empty: the kernels clamp block ids into [0, num_blocks) and cannot see lengths on the
+ *     host, so an empty pool is refused (PKV_E_INVALID_ARGUMENT) rather than risked.
  *
  * Supported: head_dim in {64, 128, 256}; num_q_heads % num_kv_heads == 0; block_size a power of
  * two from 16 to 256; bf16 data, fp32 accumulation, bf16 output rounded to nearest even.

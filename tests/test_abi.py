@@ -74,6 +74,9 @@ def test_argument_errors_return_before_launch():
     need = lib.pkv_decode_workspace_bytes(2, 8, 2, 128, 1024, 512)
     assert lib.pkv_paged_attn_decode(*dargs, 2, 8, 2, 128, 16, 64, 64, 1024, 1.0, 512, fake, need - 1, nul) \
         == pkv.E_WORKSPACE_TOO_SMALL
+    # an empty block pool is refused even on the direct path (block ids are clamped into the pool)
+    assert lib.pkv_paged_attn_decode(*dargs, 2, 8, 2, 128, 16, 0, 64, 1024, 1.0, 0, nul, 0, nul) \
+        == pkv.E_INVALID_ARGUMENT
     # scatter: bad head_dim, zero tokens is a no-op
     assert lib.pkv_reshape_and_cache(nul, nul, nul, nul, nul, 4, 2, 12, 16, 8, nul) == pkv.E_INVALID_ARGUMENT
     assert lib.pkv_reshape_and_cache(nul, nul, nul, nul, nul, 0, 2, 128, 16, 8, nul) == pkv.OK

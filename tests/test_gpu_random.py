@@ -67,7 +67,7 @@ def _draw_decode(seed: int):
                 window=window, scales=scales)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_ragged_prefill(seed):
     c = _draw_prefill(7000 + seed)
     # kv = a prefix of cached keys followed by the request's own tokens; a quarter of the requests
@@ -85,12 +85,14 @@ def test_random_ragged_prefill(seed):
     assert_parity(out.cpu(), ref, f"random ragged seed {seed}")
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_paged_prefill(seed):
     c = _draw_prefill(8000 + seed)
+    # a pool two blocks larger than the requests use (never empty: the library refuses an empty pool)
+    nb = sum((p + q + c["bs"] - 1) // c["bs"] for p, q in zip(c["prefix"], c["qo"])) + 2
     ci = chunked_prefill_inputs(8000 + seed, num_q_heads=c["hq"], num_kv_heads=c["hkv"], head_dim=c["d"],
                                 chunk_lens=c["qo"], prefix_lens=c["prefix"], block_size=c["bs"],
-                                causal=c["causal"])
+                                num_blocks=nb, causal=c["causal"])
     print(f"paged seed {seed}: D={c['d']} Hq={c['hq']} Hkv={c['hkv']} chunk={c['qo']} prefix={c['prefix']} "
           f"BS={c['bs']} causal={c['causal']}", flush=True)
     kc, vc = ci.k_cache.to(DEV), ci.v_cache.to(DEV)
@@ -106,11 +108,12 @@ def test_random_paged_prefill(seed):
     assert_parity(out.cpu(), ref, f"random paged seed {seed}")
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_decode(seed):
     c = _draw_decode(9000 + seed)
+    nb = sum((L + c["bs"] - 1) // c["bs"] for L in c["lens"]) + 2
     di = paged_decode_inputs(9000 + seed, num_q_heads=c["hq"], num_kv_heads=c["hkv"], head_dim=c["d"],
-                             seq_lens=c["lens"], block_size=c["bs"])
+                             seq_lens=c["lens"], block_size=c["bs"], num_blocks=nb)
     print(f"decode seed {seed}: D={c['d']} Hq={c['hq']} Hkv={c['hkv']} lens={c['lens']} BS={c['bs']} "
           f"pt={c['pt']} fp8={c['fp8']} window={c['window']}", flush=True)
     B, Hq = di.q.shape[0], di.q.shape[1]
