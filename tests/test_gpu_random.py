@@ -143,3 +143,98 @@ def test_random_decode(seed):
     empty = ~np.isfinite(rlse)
     assert np.array_equal(np.isneginf(got), empty), "an empty sequence's lse must be -inf, others finite"
     np.testing.assert_allclose(got[~empty], rlse[~empty], rtol=0, atol=2e-3)
+
+
+def _stream_tiles(tables, lens, bs, cap):
+    """Each table row cut into tiles of at most cap blocks (CPU int32 tensors, tile-major)."""
+    B = len(lens)
+    nt = max([-(-int(L) // (bs * cap)) for L in lens] + [0])
+    out = []
+    for i in range(nt):
+        t_tab = torch.zeros((B, cap), dtype=torch.int32)
+        t_len = torch.zeros(B, dtype=torch.int32)
+        for b, L in enumerate(lens):
+            nblk = -(-int(L) // bs)
+            blocks = tables[b, i * cap:min((i + 1) * cap, nblk)]
+            t_tab[b, :len(blocks)] = blocks
+            t_len[b] = max(0, min(int(L) - i * cap * bs, cap * bs))
+        out.append((t_tab, t_len))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_streamed_decode(seed):
+    """Decode streamed over tiles of resident blocks, the tiles in a drawn order, against the oracle's
+    streamed fold (itself pinned to one-pass decode)."""
+    rng = np.random.default_rng(11000 + seed)
+    d = int(rng.choice(HEAD_DIMS))
+    hq, hkv = _heads(rng)
+    bs = int(rng.choice(BLOCK_SIZES))
+    lens = [_length(rng, 2500, 256) for _ in range(int(rng.integers(1, 7)))]
+    cap = int(rng.choice([1, 2, 3, 8, 64]))
+    nb = sum((L + bs - 1) // bs for L in lens) + 2
+    di = paged_decode_inputs(11000 + seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seq_lens=lens,
+                             block_size=bs, num_blocks=nb)
+    tiles = _stream_tiles(di.block_tables, lens, bs, cap)
+    order = rng.permutation(len(tiles))
+    tiles = [tiles[i] for i in order]
+    print(f"streamed seed {seed}: D={d} Hq={hq} Hkv={hkv} lens={lens} BS={bs} cap={cap} tiles={len(tiles)}",
+          flush=True)
+    ref, rlse = oracle.streamed_decode(di.q, di.k_cache, di.v_cache, tiles, di.scale, return_lse=True)
+    sd = pkv.StreamedDecode(di.q.to(DEV), di.k_cache.to(DEV), di.v_cache.to(DEV), di.scale)
+    sd.begin()
+    for t_tab, t_len in tiles:
+        sd.step(t_tab.to(DEV), t_len.to(DEV))
+    lse = torch.empty(len(lens), hq, dtype=torch.float32, device=DEV)
+    out = sd.finalize(lse=lse)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu(), ref, f"random streamed seed {seed}")
+    got = lse.cpu().double().numpy()
+    empty = ~np.isfinite(rlse)
+    assert np.array_equal(np.isneginf(got), empty)
+    np.testing.assert_allclose(got[~empty], rlse[~empty], rtol=0, atol=2e-3)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_scatter(seed):
+    """reshape_and_cache into a bf16 or an fp8 cache, bit-exact: drawn head counts, head dims
+    (including ones off the power-of-two path), block sizes (including non-powers of two), and slot
+    maps with skipped (negative or past the pool) entries."""
+    rng = np.random.default_rng(12000 + seed)
+    fp8 = bool(rng.random() < 0.5)
+    d = int(rng.choice([16, 32, 48, 64, 80, 128, 256] if fp8 else [8, 24, 64, 72, 128, 256]))
+    hkv = int(rng.choice([1, 2, 3, 4, 8]))
+    bs = int(rng.choice([1, 5, 12, 16, 32, 100, 256]))
+    nb = int(rng.integers(1, 40))
+    T = int(rng.integers(0, min(nb * bs, 300) + 1))
+    slots = rng.choice(nb * bs, size=T, replace=False).astype(np.int64)
+    skip = rng.random(T) < 0.1
+    slots[skip] = np.where(rng.random(int(skip.sum())) < 0.5, -1, nb * bs + rng.integers(0, 50, int(skip.sum())))
+    slots = torch.from_numpy(slots)
+    # the library skips slots past the pool like negative ones (a caller error it tolerates); the
+    # oracle refuses them, so it sees those entries as skipped
+    ref_slots = torch.where(slots >= nb * bs, torch.full_like(slots, -1), slots)
+    g = torch.Generator().manual_seed(12000 + seed)
+    k = (torch.randn(T, hkv, d, generator=g) * 4).to(torch.bfloat16)
+    v = (torch.randn(T, hkv, d, generator=g) * 4).to(torch.bfloat16)
+    print(f"scatter seed {seed}: fp8={fp8} T={T} Hkv={hkv} D={d} BS={bs} NB={nb} skipped={int(skip.sum())}",
+          flush=True)
+    if fp8:
+        kc0 = torch.randint(0, 256, (nb, hkv, bs, d), generator=g, dtype=torch.int32).to(torch.uint8)
+        vc0 = torch.randint(0, 256, (nb, hkv, bs, d), generator=g, dtype=torch.int32).to(torch.uint8)
+        ks, vs = float(rng.choice([0.01, 0.5, 2.0])), float(rng.choice([0.02, 1.0, 3.0]))
+        ek, ev = oracle.reshape_and_cache_fp8(k, v, kc0, vc0, ref_slots, ks, vs)
+        kc, vc = kc0.to(DEV), vc0.to(DEV)
+        pkv.reshape_and_cache_fp8(k.to(DEV), v.to(DEV), kc, vc, slots.to(DEV), ks, vs)
+        torch.cuda.synchronize()
+        assert np.array_equal(kc.cpu().numpy(), ek) and np.array_equal(vc.cpu().numpy(), ev)
+    else:
+        bits = lambda: torch.randint(-32768, 32768, (nb, hkv, bs, d), generator=g,
+                                     dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+        kc0, vc0 = bits(), bits()
+        ek, ev = oracle.reshape_and_cache(k, v, kc0, vc0, ref_slots)
+        kc, vc = kc0.to(DEV), vc0.to(DEV)
+        pkv.reshape_and_cache(k.to(DEV), v.to(DEV), kc, vc, slots.to(DEV))
+        torch.cuda.synchronize()
+        assert np.array_equal(kc.cpu().view(torch.int16).numpy(), ek)
+        assert np.array_equal(vc.cpu().view(torch.int16).numpy(), ev)
