@@ -9,6 +9,7 @@ import torch
 import oracle
 import paged_kv_cache_232_amd as pkv
 from parity import assert_parity
+from test_gpu_stream import _tiles
 from workloads import chunked_prefill_inputs, paged_decode_inputs, ragged_prefill_inputs
 
 pytestmark = pytest.mark.gpu
@@ -145,23 +146,6 @@ def test_random_decode(seed):
     np.testing.assert_allclose(got[~empty], rlse[~empty], rtol=0, atol=2e-3)
 
 
-def _stream_tiles(tables, lens, bs, cap):
-    """Each table row cut into tiles of at most cap blocks (CPU int32 tensors, tile-major)."""
-    B = len(lens)
-    nt = max([-(-int(L) // (bs * cap)) for L in lens] + [0])
-    out = []
-    for i in range(nt):
-        t_tab = torch.zeros((B, cap), dtype=torch.int32)
-        t_len = torch.zeros(B, dtype=torch.int32)
-        for b, L in enumerate(lens):
-            nblk = -(-int(L) // bs)
-            blocks = tables[b, i * cap:min((i + 1) * cap, nblk)]
-            t_tab[b, :len(blocks)] = blocks
-            t_len[b] = max(0, min(int(L) - i * cap * bs, cap * bs))
-        out.append((t_tab, t_len))
-    return out
-
-
 @pytest.mark.parametrize("seed", range(16))
 def test_random_streamed_decode(seed):
     """Decode streamed over tiles of resident blocks, the tiles in a drawn order, against the oracle's
@@ -175,7 +159,7 @@ def test_random_streamed_decode(seed):
     nb = sum((L + bs - 1) // bs for L in lens) + 2
     di = paged_decode_inputs(11000 + seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seq_lens=lens,
                              block_size=bs, num_blocks=nb)
-    tiles = _stream_tiles(di.block_tables, lens, bs, cap)
+    tiles = _tiles(di.block_tables, lens, bs, cap)
     order = rng.permutation(len(tiles))
     tiles = [tiles[i] for i in order]
     print(f"streamed seed {seed}: D={d} Hq={hq} Hkv={hkv} lens={lens} BS={bs} cap={cap} tiles={len(tiles)}",
